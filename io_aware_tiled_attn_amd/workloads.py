@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs shared by the tests, the smoke entry and the bench.
+
+This module draws random numbers and rounds them to the storage type; it
+holds none of attention's arithmetic, so both the CPU oracle and the GPU
+library can be fed from it without sharing any of the method's code.
+
+Recipe (one per workload, seeded by its index):
+  rng = numpy.random.default_rng(seed)                       # PCG64
+  Q, K, V, dO = rng.standard_normal(shape, float32) x 4       # in this order
+  bf16 workloads round each float32 value to bfloat16, round-to-nearest-even.
+Values are N(0, 1) with no structure, standing in for the pages' training
+workloads (BERT, GPT-2, Long-Range Arena, Path-X), whose data is not used.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "bf16" or "fp32"
+    causal: bool
+    backward: bool      # whether the workload includes the backward pass
+    seed: int
+    what: str
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+# The five workloads: a fp32 single head, a short non-causal batch, the
+# N=4096 d=128 causal shape that the throughput metric is quoted on, a 16K
+# causal long context, and a causal forward+backward.
+WORKLOADS = {
+    "fp32_single_head": Workload(
+        "fp32_single_head", 1, 1, 256, 64, "fp32", False, False, 1,
+        "fp32 single head B1 H1 N256 d64, non-causal, forward"),
+    "bf16_n1k_d64": Workload(
+        "bf16_n1k_d64", 8, 16, 1024, 64, "bf16", False, False, 2,
+        "bf16 B8 H16 N1024 d64, non-causal, forward"),
+    "bf16_n4k_d128_causal": Workload(
+        "bf16_n4k_d128_causal", 4, 32, 4096, 128, "bf16", True, True, 3,
+        "bf16 B4 H32 N4096 d128, causal, forward and backward"),
+    "bf16_n16k_d64_causal": Workload(
+        "bf16_n16k_d64_causal", 1, 16, 16384, 64, "bf16", True, False, 4,
+        "bf16 B1 H16 N16384 d64, causal long context, forward"),
+    "bf16_n2k_d64_causal_fwdbwd": Workload(
+        "bf16_n2k_d64_causal_fwdbwd", 4, 16, 2048, 64, "bf16", True, True, 5,
+        "bf16 B4 H16 N2048 d64, causal, forward and backward"),
+}
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns as uint16.  Inputs must be finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """Exact widening of bfloat16 bit patterns (uint16) to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def draw(shape, seed, count=4):
+    """The first `count` of Q, K, V, dO as float32 N(0, 1), drawn in order."""
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal(shape, dtype=np.float32) for _ in range(count)]
+
+
+def make_inputs(shape, seed, dtype="bf16", with_grad=False):
+    """Seeded inputs for one workload shape.
+
+    Returns a dict with "q", "k", "v" (and "do" when with_grad) holding the
+    stored representation: uint16 bf16 bit patterns for dtype "bf16", float32
+    arrays for "fp32".  `values(inputs[name], dtype)` gives the exact values
+    as float32.
+    """
+    arrays = draw(tuple(shape), seed, 4 if with_grad else 3)
+    names = ["q", "k", "v", "do"][:len(arrays)]
+    if dtype == "bf16":
+        return {n: f32_to_bf16_bits(a) for n, a in zip(names, arrays)}
+    if dtype == "fp32":
+        return dict(zip(names, arrays))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def values(stored, dtype):
+    """Exact numeric values of a stored input as float32."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(stored)
+    return np.asarray(stored, dtype=np.float32)
+
+
+def workload_inputs(name, with_grad=None):
+    w = WORKLOADS[name]
+    if with_grad is None:
+        with_grad = w.backward
+    return make_inputs(w.shape, w.seed, w.dtype, with_grad)
