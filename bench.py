@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention on one MI355X: forward + backward.
+
+One step is the whole hot path once: the forward kernel (O and LSE) and the
+three backward kernels (D and dQ-accumulator set-up, the main recompute
+kernel, dQ finalisation) on one batch of seeded synthetic input already
+resident in HBM.  The default workload is B=4, H=32, N=4096, d=128, bf16,
+causal.  FLOPs follow the usual convention: forward 4*B*H*N^2*d, halved when
+causal; backward 2.5x the forward (five products, including the recomputed
+Q K^T); softmax work is not counted.
+
+Prints one JSON line (see the design doc for every field).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s and % of MI355X bf16 MFMA peak at N=4K,d=128"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published figure
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["io_aware_tiled_attn_amd/csrc/fa_fwd.hip", "io_aware_tiled_attn_amd/csrc/fa_bwd.hip",
+                  "io_aware_tiled_attn_amd/csrc/fa_common.h"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_n4k_d128_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the workload the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def flops(w):
+    fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return fwd, 2.5 * fwd
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this kernel and workload, or the kernel
+    sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(kernel, {})
+    if entry.get("workload") != workload or entry.get("source_sha") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, gpu_out, heads):
+    """Time the float64 oracle on `heads` whole heads of the same workload
+    (forward and backward), and compare the GPU results on those heads."""
+    import numpy as np
+    import oracle
+    from io_aware_tiled_attn_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    picks = [(b, h) for b in range(w.B) for h in range(w.H)][::max(1, (w.B * w.H) // heads)][:heads]
+    errs = {"o": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
+    elapsed = 0.0
+    for b, h in picks:
+        q, k, v, do = (wl.values(inp[n][b, h], w.dtype).astype(np.float64) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attention_forward_head(q, k, v, causal=w.causal)
+        dq_ref, dk_ref, dv_ref, _ = oracle.attention_backward_head(q, k, v, do, causal=w.causal)
+        elapsed += time.perf_counter() - t0
+        for name, ref in (("o", o_ref), ("lse", lse_ref), ("dq", dq_ref), ("dk", dk_ref), ("dv", dv_ref)):
+            errs[name] = max(errs[name], float(np.max(np.abs(gpu_out[name][b, h] - ref))))
+    f_fwd, f_bwd = flops(w)
+    per_head = (f_fwd + f_bwd) / (w.B * w.H)
+    return {
+        "value": per_head * len(picks) / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{len(picks)} whole heads {picks} of the same workload, forward+backward, float64 numpy "
+                  f"({elapsed:.1f} s); FLOPs counted with the GPU's convention (the oracle itself forms the "
+                  f"full masked N x N matrices)",
+        "seconds": elapsed,
+    }, errs
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): every head is independent and this "
+              "build has no multi-GPU path; see DESIGN.md for how the work would shard.", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+    import io_aware_tiled_attn_amd as fa
+    from io_aware_tiled_attn_amd import binding
+    from io_aware_tiled_attn_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = wl.WORKLOADS[args.workload]
+    if w.dtype != "bf16" or not w.backward:
+        print("the benchmark step is forward+backward in bf16", file=sys.stderr)
+        return 1
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = wl.workload_inputs(w.name, with_grad=True)
+
+    def gpu(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, do = (gpu(inp[n]) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.flash_attn_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.flash_attn_fwd(q, k, v, causal=w.causal, out=o, lse=lse)
+        if ev:
+            ev[1].record(stream)
+        kw = dict(causal=w.causal, workspace=ws, dq=dq, dk=dk, dv=dv)
+        fa.flash_attn_bwd_ex(q, k, v, o, lse, do, phases=binding.FA_BWD_PREPROCESS, **kw)
+        if ev:
+            ev[2].record(stream)
+        fa.flash_attn_bwd_ex(q, k, v, o, lse, do, phases=binding.FA_BWD_MAIN, **kw)
+        if ev:
+            ev[3].record(stream)
+        fa.flash_attn_bwd_ex(q, k, v, o, lse, do, phases=binding.FA_BWD_FINALIZE, **kw)
+        if ev:
+            ev[4].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    fin_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+
+    f_fwd, f_bwd = flops(w)
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = f_fwd / (fwd_ms * 1e-3) / 1e12
+    bwd_ms = prep_ms + main_ms + fin_ms
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+    main_tf = f_bwd / (main_ms * 1e-3) / 1e12
+    # Dominant kernel of the step: the one with the larger share of time.
+    if main_ms >= fwd_ms:
+        dom, dom_ms, dom_flops = "fa_bwd_main_kernel", main_ms, f_bwd
+    else:
+        dom, dom_ms, dom_flops = "fa_fwd_bf16_kernel", fwd_ms, f_fwd
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = measured_traffic(dom, w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q, K, V, dO (numpy PCG64, seed %d), rounded to bf16" % w.seed,
+        "config": {"workload": "attention forward+backward, B=%d H=%d N=%d d=%d, bf16, %s"
+                               % (w.B, w.H, w.N, w.d, "causal" if w.causal else "non-causal"),
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N},
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
+                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+                "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                "kernels_ms": {"preprocess": round(prep_ms, 4), "main": round(main_ms, 4),
+                               "finalize": round(fin_ms, 4)},
+                "main_kernel_tflops": round(main_tf, 2)},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "peak_basis": "MI355X dense bf16 MFMA 2.5 PFLOP/s (published); FLOPs: fwd 4BHN^2d (x1/2 causal), "
+                      "bwd 2.5x fwd",
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
+        gpu_out = {"o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.float().cpu().numpy(),
+                   "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy()}
+        base, errs = cpu_baseline(w, inp, gpu_out, args.cpu_heads)
+        result["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2)
+                                  for k2, v2 in base.items() if k2 != "seconds"}
+        result["sample_max_abs_err"] = {k2: float("%.3e" % v2) for k2, v2 in errs.items()}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,172 @@
+/*
+ * flash_attn.h - exact tiled attention (FlashAttention) on AMD Instinct
+ * MI355X (gfx950): the C ABI of libflash_attn.so.
+ *
+ * What is computed.  For every batch b and head h, with Q, K, V the
+ * [N, d] slices of that head,
+ *     S = scale * Q K^T          (causal: S_ij = -inf where key j > query i)
+ *     P = softmax(S) row by row  (safe softmax: subtract the row max m_i,
+ *                                 exponentiate, divide by the row sum l_i)
+ *     O = P V,   LSE_i = m_i + ln(l_i)
+ * This is the standard attention of "FlashAttention, explained"
+ * (vibeengines.com), sections "The math, worked with real numbers" and
+ * "Solve it yourself", which divides the scores by sqrt(d); here the factor
+ * is the explicit argument `scale`.  The forward kernel walks the keys tile
+ * by tile and keeps a running max, a running sum and a rescaled output
+ * accumulator per query row (same page, section "Tiling and the online
+ * softmax"), so the N x N matrix S is never written to memory; the extra
+ * memory is O and LSE only (chorfi.xyz study guide, "Guarantees versus
+ * empirical results": extra memory linear in N).  The backward pass
+ * recomputes the score tiles from LSE instead of storing P (chorfi.xyz,
+ * "Study objectives"; modelfieldguide.com, "An IO-aware rewrite").
+ *
+ * Conventions shared by every entry point.
+ *   - Pointers are device pointers (hipMalloc'd or torch CUDA tensors) owned
+ *     by the caller.  The library never allocates or frees device memory.
+ *   - Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d]
+ *     (the element of (b, h, n, c) sits at ((b*H + h)*N + n)*d + c) in the
+ *     element type `dtype`.  LSE is contiguous [B, H, N] float32.
+ *     Base pointers must be 16-byte aligned.  Outputs must not alias inputs.
+ *   - Supported: B >= 1, H >= 1, N >= 1 (any N; the tail tile is masked),
+ *     d in {64, 128}, finite scale > 0, causal in {0, 1}.  Causal masks key
+ *     j > query i, with queries and keys aligned at index 0.
+ *   - dtype FA_DTYPE_BF16: bfloat16 storage, fp32 accumulation inside the
+ *     kernels, round-to-nearest-even on every narrowing.  FA_DTYPE_FP32:
+ *     float32 storage and float32 arithmetic throughout (forward only).
+ *   - B*H*N*d must stay below 2^31 elements per tensor.
+ *   - stream is a hipStream_t; NULL means the default stream.  Every call is
+ *     asynchronous: it validates its arguments, enqueues kernels on `stream`
+ *     and returns.  Faults during execution surface at the caller's next
+ *     synchronisation of that stream.
+ *   - Errors: arguments are checked before any HIP call; a bad argument
+ *     returns FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED with nothing enqueued.
+ *     A failed launch returns FA_ERR_HIP.  No exception crosses the ABI.
+ *   - The functions keep no state between calls and may be called from
+ *     several host threads.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad flag  */
+    FA_ERR_UNSUPPORTED = 2,  /* valid request this library does not serve */
+    FA_ERR_HIP = 3           /* the HIP runtime rejected a launch          */
+};
+
+enum fa_dtype {
+    FA_DTYPE_BF16 = 0,
+    FA_DTYPE_FP32 = 1
+};
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [causal mask]) V and the per-row
+ * natural-log LSE, the definition above evaluated by the online-softmax
+ * update rule of vibeengines.com "The math, worked with real numbers":
+ * m_new = max(m_old, block max); l_new = l_old e^(m_old - m_new) + sum of
+ * e^(s - m_new); O_new = O_old e^(m_old - m_new) + sum of e^(s - m_new) V;
+ * result O / l.
+ *   q, k, v : [B, H, N, d] dtype, read only.
+ *   o       : [B, H, N, d] dtype, written.
+ *   lse     : [B, H, N] float32, written (may be NULL to skip it).
+ * Returns FA_OK, FA_ERR_INVALID_ARG (null q/k/v/o, B/H/N < 1, scale not
+ * finite and > 0, causal not 0/1, misaligned pointer, too many elements),
+ * FA_ERR_UNSUPPORTED (d not 64/128, unknown dtype) or FA_ERR_HIP.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v,
+                   void* o, float* lse,
+                   int B, int H, int N, int d,
+                   float scale, int causal, int dtype, void* stream);
+
+/*
+ * Same as flash_attn_fwd with the key-tile width forced: block_n = 0 picks
+ * the default, otherwise 32, 64 or 128 keys per tile (bf16 only; the fp32
+ * path accepts 0 or 32).  The result must not depend on it (vibeengines.com,
+ * "Solve it yourself": the block size never changes the answer); tests use
+ * it to check that.  Other values return FA_ERR_UNSUPPORTED.
+ */
+int flash_attn_fwd_ex(const void* q, const void* k, const void* v,
+                      void* o, float* lse,
+                      int B, int H, int N, int d,
+                      float scale, int causal, int dtype, void* stream,
+                      int block_n);
+
+/*
+ * Bytes of device workspace flash_attn_bwd needs: an fp32 dQ accumulator
+ * [B, H, N, d] and the fp32 row terms D_i = sum_c dO_ic O_ic [B, H, N],
+ * i.e. 4*B*H*N*(d+1) bytes rounded up to 256, linear in N.  Returns 0 for
+ * invalid sizes.
+ */
+size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass: gradients of O with respect to Q, K and V for the
+ * upstream gradient dO, recomputing each score tile from Q, K and the saved
+ * LSE (P = exp(scale * q.k - LSE)) instead of reading a stored P.  The
+ * gradient formulas are the calculus of the forward definition:
+ *     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+ *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, o, dout : [B, H, N, d] bf16, read only (o, lse from the
+ *                      forward pass with the same scale and causal flag).
+ *   lse              : [B, H, N] float32.
+ *   dq, dk, dv       : [B, H, N, d] bf16, written.
+ *   workspace        : device buffer of at least
+ *                      flash_attn_bwd_workspace_size(B, H, N, d) bytes,
+ *                      256-byte aligned, owned by the caller; its contents
+ *                      on entry do not matter and are clobbered.
+ * dtype must be FA_DTYPE_BF16 (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED).
+ * Other errors as for flash_attn_fwd, plus FA_ERR_INVALID_ARG for a null
+ * or short workspace.
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v,
+                   const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d,
+                   float scale, int causal, int dtype, void* stream);
+
+/*
+ * flash_attn_bwd split into its three kernels, for callers that time or
+ * schedule them separately.  `phases` is a bit mask:
+ *   FA_BWD_PREPROCESS (1): D_i = sum_c dO_ic O_ic into the workspace and
+ *                          zero the workspace's fp32 dQ accumulator;
+ *   FA_BWD_MAIN       (2): recompute P tile by tile, write dK and dV, add
+ *                          dQ (unscaled) into the accumulator;
+ *   FA_BWD_FINALIZE   (4): dq = scale * accumulator, rounded to bf16.
+ * Running the phases in that order, on one stream, with the same arguments
+ * and workspace, equals one flash_attn_bwd call (phases = 7).  A mask of 0
+ * or with other bits returns FA_ERR_INVALID_ARG.  Other arguments and errors
+ * as for flash_attn_bwd.
+ */
+enum fa_bwd_phase {
+    FA_BWD_PREPROCESS = 1,
+    FA_BWD_MAIN = 2,
+    FA_BWD_FINALIZE = 4,
+    FA_BWD_ALL = 7
+};
+
+int flash_attn_bwd_ex(const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d,
+                      float scale, int causal, int dtype, void* stream,
+                      int phases);
+
+/* Static, never-NULL description of a status code (unknown codes included). */
+const char* flash_attn_status_string(int status);
+
+/* Text of the last HIP error seen by a call on this host thread ("" if none). */
+const char* flash_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

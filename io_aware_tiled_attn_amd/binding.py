@@ -1,0 +1,197 @@
+"""ctypes binding of libflash_attn.so (include/flash_attn.h).
+
+Argument marshalling only: shape, dtype, device and contiguity checks,
+allocation of the outputs with torch, and the current torch stream.  Every
+step of the attention computation runs in the library's HIP kernels; there is
+no fallback.  If the library has not been built, the first call raises.
+"""
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libflash_attn.so"
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+FA_DTYPE_BF16 = 0
+FA_DTYPE_FP32 = 1
+FA_BWD_PREPROCESS = 1
+FA_BWD_MAIN = 2
+FA_BWD_FINALIZE = 4
+FA_BWD_ALL = 7
+
+_lib = None
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {flash_attn_status_string(status)} (status {status})"
+                         + (f" [{_raw().flash_attn_last_hip_error().decode()}]"
+                            if status == FA_ERR_HIP else ""))
+
+
+def library_path():
+    return os.path.join(PKG_DIR, LIB_NAME)
+
+
+def _raw():
+    """The loaded CDLL with argument and result types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m io_aware_tiled_attn_amd.build` "
+            "(there is no non-HIP implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_fwd.restype = i
+    lib.flash_attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, i]
+    lib.flash_attn_fwd_ex.restype = i
+    lib.flash_attn_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.flash_attn_bwd_workspace_size.restype = sz
+    lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd.restype = i
+    lib.flash_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp, i]
+    lib.flash_attn_bwd_ex.restype = i
+    lib.flash_attn_status_string.argtypes = [i]
+    lib.flash_attn_status_string.restype = ctypes.c_char_p
+    lib.flash_attn_last_hip_error.argtypes = []
+    lib.flash_attn_last_hip_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def flash_attn_status_string(status):
+    return _raw().flash_attn_status_string(int(status)).decode()
+
+
+def flash_attn_bwd_workspace_size(B, H, N, d):
+    return int(_raw().flash_attn_bwd_workspace_size(int(B), int(H), int(N), int(d)))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_FP32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def flash_attn_fwd_ex(q, k, v, causal=False, scale=None, block_n=0, out=None, lse=None, stream=None):
+    """Forward pass on [B, H, N, d] tensors; returns (O, LSE).
+
+    q, k, v: contiguous GPU tensors, bfloat16 or float32, same shape.
+    scale defaults to 1/sqrt(d).  LSE is float32 [B, H, N].
+    block_n forces the key-tile width (0 = default).
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, q.shape)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.dtype, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  B, H, N, d, float(scale), int(bool(causal)), code, _stream_ptr(stream),
+                                  int(block_n))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd")
+    return out, lse
+
+
+def flash_attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """Forward pass; see flash_attn_fwd_ex."""
+    return flash_attn_fwd_ex(q, k, v, causal=causal, scale=scale, block_n=0, out=out, lse=lse, stream=stream)
+
+
+def flash_attn_bwd_ex(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, stream=None,
+                      dq=None, dk=None, dv=None, phases=FA_BWD_ALL):
+    """Backward pass (bfloat16); returns (dQ, dK, dV).
+
+    o and lse come from flash_attn_fwd with the same causal flag and scale.
+    workspace, if given, is a uint8 GPU tensor of at least
+    flash_attn_bwd_workspace_size(B, H, N, d) bytes; otherwise one is
+    allocated with torch for this call.  `phases` selects which of the three
+    backward kernels run (FA_BWD_* bits); callers running them one at a time
+    pass the same workspace and output tensors to each call.
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (B, H, N))
+    need = flash_attn_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check(t, name, q.dtype, q.shape)
+        outs.append(t)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                  workspace.data_ptr(), workspace.numel(), B, H, N, d, float(scale),
+                                  int(bool(causal)), code, _stream_ptr(stream), int(phases))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd")
+    return tuple(outs)
+
+
+def flash_attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, stream=None,
+                   dq=None, dk=None, dv=None):
+    """Backward pass (all three kernels); see flash_attn_bwd_ex."""
+    return flash_attn_bwd_ex(q, k, v, o, lse, do, causal=causal, scale=scale, workspace=workspace,
+                             stream=stream, dq=dq, dk=dk, dv=dv, phases=FA_BWD_ALL)

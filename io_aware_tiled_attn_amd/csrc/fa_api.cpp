@@ -1,0 +1,117 @@
+// C-ABI entry points of libflash_attn.so: argument validation (no HIP call
+// before it passes), dispatch to the kernel launchers, status reporting.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  const char* s = hipGetErrorString(e);
+  std::strncpy(g_last_hip_error, s ? s : "unknown HIP error", sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest element count of one [B, H, N, d] tensor the kernels index with
+// 32-bit row arithmetic inside a head and 64-bit offsets across heads.
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+int check_sizes(int B, int H, int N, int d, float scale, int causal) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N * d > kMaxElems) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             float scale, int causal, int dtype, void* stream, int block_n) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_BF16 && block_n != 0 && block_n != 32 && block_n != 64 && block_n != 128)
+    return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_FP32 && block_n != 0 && block_n != 32) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_n, (hipStream_t)stream};
+  return hip_status(fa::launch_fwd(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, 0);
+}
+
+int flash_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                      int d, float scale, int causal, int dtype, void* stream, int block_n) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, block_n);
+}
+
+size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  if ((long long)B * H * N * d > kMaxElems) return 0;
+  const size_t rows = (size_t)B * H * N;
+  const size_t acc = rows * (size_t)d * 4;           // fp32 dQ accumulator
+  const size_t acc_padded = (acc + 255) & ~(size_t)255;
+  const size_t bytes = acc_padded + rows * 4;        // fp32 D per row
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int flash_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                      int H, int N, int d, float scale, int causal, int dtype, void* stream, int phases) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  if (phases <= 0 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  const size_t need = flash_attn_bwd_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * N;
+  const size_t acc_padded = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
+  float* dq_acc = static_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_padded);
+  fa::BwdArgs a{q,     k,     v, o,      dout,   lse,   dq,     dk,    dv, dq_acc,
+                delta, B,     H, N,      d,      scale, causal, phases, (hipStream_t)stream};
+  return hip_status(fa::launch_bwd(a));
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, void* stream) {
+  return flash_attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                           dtype, stream, FA_BWD_ALL);
+}
+
+const char* flash_attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* flash_attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

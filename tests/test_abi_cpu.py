@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments before touching the GPU (no call here
+reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from io_aware_tiled_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+lib_missing = not os.path.exists(binding.library_path())
+pytestmark = pytest.mark.skipif(lib_missing, reason="libflash_attn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(flash_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(["flash_attn_fwd", "flash_attn_fwd_ex", "flash_attn_bwd", "flash_attn_bwd_ex",
+                            "flash_attn_bwd_workspace_size", "flash_attn_status_string",
+                            "flash_attn_last_hip_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(binding._raw(), name)
+
+
+def test_status_strings_never_null():
+    for code in (-5, 0, 1, 2, 3, 4, 1000):
+        s = binding.flash_attn_status_string(code)
+        assert isinstance(s, str) and s
+    assert binding.flash_attn_status_string(0) == "ok"
+
+
+def test_workspace_size_is_linear_in_n():
+    f = binding.flash_attn_bwd_workspace_size
+    assert f(4, 32, 4096, 128) >= 4 * 4 * 32 * 4096 * 129
+    assert f(4, 32, 4096, 128) % 256 == 0
+    assert f(1, 1, 2048, 64) * 2 - f(1, 1, 4096, 64) < 1024
+    assert f(0, 1, 1, 64) == 0 and f(1, 1, -1, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)       # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, scale=0.125,
+             causal=0, dtype=binding.FA_DTYPE_BF16, stream=None, block_n=0)
+    a.update(kw)
+    return binding._raw().flash_attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                            a["d"], a["scale"], a["causal"], a["dtype"], a["stream"],
+                                            a["block_n"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(B=0), binding.FA_ERR_INVALID_ARG),
+    (dict(H=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+    (dict(k=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+    (dict(B=4096, H=4096, N=4096), binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(d=256), binding.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), binding.FA_ERR_UNSUPPORTED),
+    (dict(block_n=48), binding.FA_ERR_UNSUPPORTED),
+    (dict(block_n=64, dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+])
+def test_forward_rejects_bad_arguments(kw, code):
+    assert fwd(**kw) == code
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 40, B=1, H=1, N=16, d=64, scale=0.125, causal=1,
+             dtype=binding.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                                         a["dv"], a["ws"], a["ws_bytes"], a["B"], a["H"], a["N"], a["d"],
+                                         a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ws=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), binding.FA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x10010)), binding.FA_ERR_INVALID_ARG),
+    (dict(dv=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(d=32), binding.FA_ERR_UNSUPPORTED),
+    (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+])
+def test_backward_rejects_bad_arguments(kw, code):
+    assert bwd(**kw) == code
+
+
+@pytest.mark.parametrize("phases", [0, 8, -1, 15])
+def test_backward_rejects_bad_phase_masks(phases):
+    a = [FAKE] * 9 + [ctypes.c_void_p(0x10000), 1 << 40, 1, 1, 16, 64, 0.125, 1, binding.FA_DTYPE_BF16, None,
+                      phases]
+    assert binding._raw().flash_attn_bwd_ex(*a) == binding.FA_ERR_INVALID_ARG
+
+
+def test_python_binding_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.flash_attn_fwd(q, q, q)
