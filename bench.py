@@ -40,7 +40,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bf16_n4k_d128_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2,
+    ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the workload the CPU oracle is timed on")
     return ap.parse_args()
 

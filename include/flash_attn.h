@@ -112,8 +112,12 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d);
  * gradient formulas are the calculus of the forward definition:
  *     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
  *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * P and dS enter the dV, dK and dQ products as two bf16 terms each (the
+ * rounded value and its residual), so the products see them to 16
+ * significant bits; accumulation is fp32.
  *   q, k, v, o, dout : [B, H, N, d] bf16, read only (o, lse from the
- *                      forward pass with the same scale and causal flag).
+ *                      forward pass with the same scale and causal flag;
+ *                      D is formed from this bf16 o).
  *   lse              : [B, H, N] float32.
  *   dq, dk, dv       : [B, H, N, d] bf16, written.
  *   workspace        : device buffer of at least

@@ -90,8 +90,8 @@ int flash_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o
   const size_t acc_padded = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
   float* dq_acc = static_cast<float*>(workspace);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_padded);
-  fa::BwdArgs a{q,     k,     v, o,      dout,   lse,   dq,     dk,    dv, dq_acc,
-                delta, B,     H, N,      d,      scale, causal, phases, (hipStream_t)stream};
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dq_acc, delta, B, H, N, d, scale, causal, phases,
+                (hipStream_t)stream};
   return hip_status(fa::launch_bwd(a));
 }
 

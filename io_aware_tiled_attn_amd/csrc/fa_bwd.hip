@@ -10,7 +10,8 @@
 //     dQ = scale dS K,         dK = scale dS^T Q.
 //
 // Three kernels on one stream:
-//   1. bwd_prep: D_i = <dO_i, O_i> in fp32, and zero the fp32 dQ accumulator.
+//   1. bwd_prep: D_i = <dO_i, O_i> in fp32 from the bf16 O, and zero the fp32
+//      dQ accumulator.
 //   2. bwd_main: one workgroup of 4 waves per 128-key tile of one head.  Each
 //      wave keeps its 32 keys' K and V rows in registers (the B operands of
 //      S = Q K^T and dP = dO V^T, so each lane owns one key column of the
@@ -20,7 +21,10 @@
 //      transposed A operands with ds_read_b64_tr_b16.  dS goes through LDS
 //      once (as dS^T) so that dQ = dS K can be formed for the tile, and each
 //      wave adds its 32 x 32 block of dQ to the fp32 accumulator with
-//      hardware float atomics.
+//      hardware float atomics.  P and dS enter the dV, dK and dQ products as
+//      two bf16 terms each (rounded value + residual): one bf16 term alone
+//      leaves a relative error of up to 2^-9 per element, which at N = 4096
+//      costs up to ~8e-3 absolute in the gradients.
 //   3. bwd_dq_finalize: dQ = scale * accumulator, rounded to bf16.
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -70,10 +74,10 @@ struct BwdCfg {
   static constexpr int kKtPitch = BN + 8;        // K^T rows in LDS
   static constexpr int kDsPitch = BM + 8;        // dS^T rows in LDS
   static constexpr int kTile = BM * kRowPitch;   // elements of one Q or dO tile
-  // LDS layout (bytes): K^T | stage 0 (Q, dO, lse, delta) | stage 1 | dS^T
+  // LDS layout (bytes): K^T | stage 0 (Q, dO, lse, delta) | stage 1 | dS^T hi | dS^T lo
   static constexpr int kKtBytes = D * kKtPitch * 2;
   static constexpr int kStageBytes = 2 * kTile * 2 + 2 * BM * 4;
-  static constexpr int kDsBytes = BN * kDsPitch * 2;
+  static constexpr int kDsBytes = 2 * BN * kDsPitch * 2;   // hi and lo terms
   static constexpr int kLdsBytes = kKtBytes + 2 * kStageBytes + kDsBytes;
   static constexpr int kChunks = BM * D / 8;     // 16-byte chunks per Q tile
   static constexpr int kChunksPerThread = kChunks / kThreads;
@@ -162,7 +166,8 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   __bf16* Kt = (__bf16*)smem_raw;                                  // [D][kKtPitch]
   char* stages = smem_raw + C::kKtBytes;
-  __bf16* dSt = (__bf16*)(stages + 2 * C::kStageBytes);            // [BN][kDsPitch]
+  __bf16* dSt = (__bf16*)(stages + 2 * C::kStageBytes);            // [BN][kDsPitch], hi term
+  __bf16* dSt_lo = dSt + C::BN * C::kDsPitch;                      // lo term
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -241,9 +246,10 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
       s = mfma32(qa, kb[ks], s);
       dp = mfma32(ga, vb[ks], dp);
     }
-    // P = exp2(s * scale * log2 e - LSE * log2 e); dS = P (dP - D).
+    // P = exp2(s * scale * log2 e - LSE * log2 e); dS = P (dP - D).  Each is
+    // kept as a bf16 pair (rounded value, rounded residual).
     const bool diag = CAUSAL && (q0 < k0 + wave * 32 + 31);
-    uint32_t pw[8], dsw[8];
+    uint32_t pw[8], pl[8], dsw[8], dsl[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *(const f32x4*)(Ls + 8 * i + 4 * lg);
@@ -258,22 +264,28 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
         p[j] = pv;
         ds[j] = pv * (dp[r] - d4[j]);
       }
-      pw[2 * i] = pack_bf16x2(p[0], p[1]);
-      pw[2 * i + 1] = pack_bf16x2(p[2], p[3]);
-      dsw[2 * i] = pack_bf16x2(ds[0], ds[1]);
-      dsw[2 * i + 1] = pack_bf16x2(ds[2], ds[3]);
-      // dS^T[key][q .. q+3] for the dQ product.
-      u32x2 w2 = {dsw[2 * i], dsw[2 * i + 1]};
-      *(u32x2*)(dSt + (wave * 32 + lc) * C::kDsPitch + 8 * i + 4 * lg) = w2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t ph = pack_bf16x2(p[2 * h], p[2 * h + 1]);
+        const uint32_t dh = pack_bf16x2(ds[2 * h], ds[2 * h + 1]);
+        pw[2 * i + h] = ph;
+        pl[2 * i + h] = pack_bf16x2(p[2 * h] - bf16_lo(ph), p[2 * h + 1] - bf16_hi(ph));
+        dsw[2 * i + h] = dh;
+        dsl[2 * i + h] = pack_bf16x2(ds[2 * h] - bf16_lo(dh), ds[2 * h + 1] - bf16_hi(dh));
+      }
+      // dS^T[key][q .. q+3] (both terms) for the dQ product.
+      const int off = (wave * 32 + lc) * C::kDsPitch + 8 * i + 4 * lg;
+      *(u32x2*)(dSt + off) = (u32x2){dsw[2 * i], dsw[2 * i + 1]};
+      *(u32x2*)(dSt_lo + off) = (u32x2){dsl[2 * i], dsl[2 * i + 1]};
     }
     // B operands (k = query, in the accumulator's lane order).
-    bf16x8 pB[2], dsB[2];
+    bf16x8 pB[2], pBl[2], dsB[2], dsBl[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      u32x4 a = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
-      u32x4 b = {dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]};
-      pB[c] = __builtin_bit_cast(bf16x8, a);
-      dsB[c] = __builtin_bit_cast(bf16x8, b);
+      pB[c] = __builtin_bit_cast(bf16x8, ((u32x4){pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]}));
+      pBl[c] = __builtin_bit_cast(bf16x8, ((u32x4){pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]}));
+      dsB[c] = __builtin_bit_cast(bf16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
+      dsBl[c] = __builtin_bit_cast(bf16x8, ((u32x4){dsl[4 * c], dsl[4 * c + 1], dsl[4 * c + 2], dsl[4 * c + 3]}));
     }
     // dV^T += dO^T P and dK^T += Q^T dS (A operands read down the columns).
 #pragma unroll
@@ -284,7 +296,9 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
         const bf16x8 ga = lds_read_down(Gs, C::kRowPitch, 32 * dm, r_lo, r_hi, lane);
         const bf16x8 qa = lds_read_down(Qs, C::kRowPitch, 32 * dm, r_lo, r_hi, lane);
         dv_acc[dm] = mfma32(ga, pB[c], dv_acc[dm]);
+        dv_acc[dm] = mfma32(ga, pBl[c], dv_acc[dm]);
         dk_acc[dm] = mfma32(qa, dsB[c], dk_acc[dm]);
+        dk_acc[dm] = mfma32(qa, dsBl[c], dk_acc[dm]);
       }
     }
     if (qt + 1 < qt_end) bwd_store_stage<D>(st, stages + ((it + 1) & 1) * C::kStageBytes, tid);
@@ -304,8 +318,10 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
       for (int j = 0; j < kSteps; ++j) {
         const int kk = (kgrp * kSteps + j) * 16;
         const bf16x8 a = lds_read_down(dSt, C::kDsPitch, 0, kk + 8 * lg, kk + 8 * lg + 4, lane);
+        const bf16x8 al = lds_read_down(dSt_lo, C::kDsPitch, 0, kk + 8 * lg, kk + 8 * lg + 4, lane);
         const bf16x8 b = *(const bf16x8*)(Kt + (32 * dm + lc) * C::kKtPitch + kk + 8 * lg);
         acc = mfma32(a, b, acc);
+        acc = mfma32(al, b, acc);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

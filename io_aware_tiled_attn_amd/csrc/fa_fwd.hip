@@ -252,7 +252,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   }
 
-  // Epilogue: O / l and LSE = m + ln l (natural log).
+  // Epilogue: O / l rounded to bf16, and LSE = m + ln l (natural log).
   const float l_tot = sum_with_lane_xor32(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_idx < N) {

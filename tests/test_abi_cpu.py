@@ -86,6 +86,7 @@ def fwd(**kw):
     (dict(dtype=7), binding.FA_ERR_UNSUPPORTED),
     (dict(block_n=48), binding.FA_ERR_UNSUPPORTED),
     (dict(block_n=64, dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+    (dict(lse=MISALIGNED), binding.FA_ERR_INVALID_ARG),
 ])
 def test_forward_rejects_bad_arguments(kw, code):
     assert fwd(**kw) == code
@@ -112,6 +113,7 @@ def bwd(**kw):
     (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
     (dict(d=32), binding.FA_ERR_UNSUPPORTED),
     (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+    (dict(o=MISALIGNED), binding.FA_ERR_INVALID_ARG),
 ])
 def test_backward_rejects_bad_arguments(kw, code):
     assert bwd(**kw) == code
