@@ -42,6 +42,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB once (device to device) so that "
+                         "HBM byte counters can be scaled against a transfer of known size")
     return ap.parse_args()
 
 
@@ -158,6 +161,12 @@ def main():
         if ev:
             ev[4].record(stream)
 
+    if args.calibrate_copy_mb:
+        src = torch.ones(args.calibrate_copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

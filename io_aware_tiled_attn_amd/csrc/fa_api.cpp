@@ -41,7 +41,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERR_INVALID_ARG;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
-  if (dtype == FA_DTYPE_BF16 && block_n != 0 && block_n != 32 && block_n != 64 && block_n != 128)
+  if (dtype == FA_DTYPE_BF16 && block_n != 0 && block_n != 32 && block_n != 64)
     return FA_ERR_UNSUPPORTED;
   if (dtype == FA_DTYPE_FP32 && block_n != 0 && block_n != 32) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_n, (hipStream_t)stream};

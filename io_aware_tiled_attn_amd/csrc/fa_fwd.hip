@@ -4,29 +4,43 @@
 // update (vibeengines.com "FlashAttention, explained", sections "Tiling and
 // the online softmax" and "The math, worked with real numbers"): for each
 // query row keep a running max m, a running sum l and an output accumulator
-// O; for each new key tile, m_new = max(m, tile max), rescale l and O by
-// e^(m - m_new), add the tile's e^(s - m_new) and e^(s - m_new) V; finish
-// with O / l.  The N x N scores never leave registers.
+// O; for each new key tile rescale l and O by e^(m_old - m_new) and add the
+// tile's e^(s - m) and e^(s - m) V; finish with O / l.  The N x N scores
+// never leave registers.
 //
 // bf16 kernel layout (one workgroup = 8 waves = 256 query rows):
 //   * each wave owns 32 consecutive queries; its Q slice lives in registers
 //     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so the
 //     32x32 accumulator puts one query per lane column: the row max and row
 //     sum are in-lane reductions plus one permlane32 swap.
-//   * K and V tiles of BN keys are staged in LDS, double buffered, shared by
-//     the 8 waves.  K is stored row-major with padding; V is stored
-//     transposed (V^T[d][key]) with the keys of each 16-key group reordered
-//     so the A operand of O^T += V^T P^T is one 16-byte LDS read per lane
-//     and matches the key order the S^T accumulator leaves in each lane.
+//   * K and V tiles of BN keys are staged in LDS and shared by the 8 waves.
+//     K runs one tile ahead of V: while a wave turns tile t's scores into
+//     probabilities (VALU, exp2) it already issues the MFMAs of tile t+1's
+//     scores, so the matrix cores and the vector ALU overlap inside a wave
+//     as well as across the two waves sharing a SIMD.  Double buffers for K
+//     and for V with one barrier per tile.
+//   * K is stored row-major with padding; V is stored transposed
+//     (V^T[d][key]) with the keys of each 16-key group reordered so that the
+//     A operand of O^T += V^T P^T is one 16-byte LDS read per lane and
+//     matches the key order the S^T accumulator leaves in each lane.
 //   * P is rounded to bf16 (RNE) and fed back as the B operand directly from
 //     the accumulator registers; O^T accumulates in fp32.
-//   * workgroups are issued heaviest first (causal), with all query tiles of
+//   * The running max is raised only when a tile's max exceeds it by more
+//     than kMaxSlack (log2 units).  Any reference value works in exact
+//     arithmetic (it cancels in O / l); keeping it within 2^kMaxSlack of the
+//     true max keeps every P <= 2^kMaxSlack, and the output rescale becomes
+//     rare instead of happening on almost every tile.
+//   * Global reads use buffer descriptors sized to the head: reads past the
+//     last row return zeros, so ragged tails need no branches.
+//   * Workgroups are issued heaviest first (causal), with all query tiles of
 //     one head on the same XCD (dispatch is round-robin over 8 XCDs and the
 //     head index is the fast-varying part of the workgroup id).
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+constexpr float kMaxSlack = 8.0f;
 
 template <int D, int BN>
 struct FwdCfg {
@@ -37,8 +51,8 @@ struct FwdCfg {
   static constexpr int kVPitch = BN + 8;   // bf16 elements per V^T row in LDS
   static constexpr int kKTile = BN * kKPitch;
   static constexpr int kVTile = D * kVPitch;
-  static constexpr int kStage = kKTile + kVTile;
-  static constexpr int kLdsBytes = 2 * kStage * 2;
+  // LDS: K buffer 0 | K buffer 1 | V^T buffer 0 | V^T buffer 1
+  static constexpr int kLdsBytes = 2 * (kKTile + kVTile) * 2;
   static constexpr int kKChunks = BN * D / 8;             // 16-byte K chunks
   static constexpr int kKPerThread = (kKChunks + kThreads - 1) / kThreads;
   static constexpr int kVBlocks = (BN / 4) * (D / 4);     // 4x4 V blocks
@@ -54,62 +68,81 @@ __device__ __forceinline__ int vt_key_slot(int k) {
   return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// Buffer descriptor over `bytes` bytes at p (raw, 32-bit data format):
+// loads at offsets >= bytes return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 template <int D, int BN>
-struct FwdStage {
+struct KStage {
   u32x4 k[FwdCfg<D, BN>::kKPerThread];
+};
+template <int D, int BN>
+struct VStage {
   u32x2 v[FwdCfg<D, BN>::kVPerThread][4];
 };
 
 template <int D, int BN>
-__device__ __forceinline__ void fwd_load_tile(FwdStage<D, BN>& st, const __bf16* __restrict__ Kh,
-                                              const __bf16* __restrict__ Vh, int j0, int N, int tid) {
+__device__ __forceinline__ void load_k_tile(KStage<D, BN>& st, __amdgpu_buffer_rsrc_t rk, int j0, int tid) {
   using C = FwdCfg<D, BN>;
 #pragma unroll
   for (int i = 0; i < C::kKPerThread; ++i) {
     const int c = tid + i * C::kThreads;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    const int key = j0 + row;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (c < C::kKChunks && key < N) val = *(const u32x4*)(Kh + (size_t)key * D + col);
-    st.k[i] = val;
+    if (C::kKChunks % C::kThreads == 0 || c < C::kKChunks)
+      st.k[i] = bload128(rk, (uint32_t)((j0 + row) * D + col) * 2u);
   }
+}
+
+template <int D, int BN>
+__device__ __forceinline__ void store_k_tile(const KStage<D, BN>& st, __bf16* Ks, int tid) {
+  using C = FwdCfg<D, BN>;
 #pragma unroll
-  for (int i = 0; i < C::kVPerThread; ++i) {
-    const int b = tid + i * C::kThreads;
-    const int kb = b / (D / 4), db = b % (D / 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = j0 + 4 * kb + r;
-      u32x2 val = {0u, 0u};
-      if (b < C::kVBlocks && key < N) val = *(const u32x2*)(Vh + (size_t)key * D + 4 * db);
-      st.v[i][r] = val;
+  for (int i = 0; i < C::kKPerThread; ++i) {
+    const int c = tid + i * C::kThreads;
+    if (C::kKChunks % C::kThreads == 0 || c < C::kKChunks) {
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *(u32x4*)(Ks + row * C::kKPitch + col) = st.k[i];
     }
   }
 }
 
 template <int D, int BN>
-__device__ __forceinline__ void fwd_store_tile(const FwdStage<D, BN>& st, __bf16* Ks, __bf16* Vts, int tid) {
+__device__ __forceinline__ void load_v_tile(VStage<D, BN>& st, __amdgpu_buffer_rsrc_t rv, int j0, int tid) {
   using C = FwdCfg<D, BN>;
-#pragma unroll
-  for (int i = 0; i < C::kKPerThread; ++i) {
-    const int c = tid + i * C::kThreads;
-    if (c < C::kKChunks) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)(Ks + row * C::kKPitch + col) = st.k[i];
-    }
-  }
 #pragma unroll
   for (int i = 0; i < C::kVPerThread; ++i) {
     const int b = tid + i * C::kThreads;
-    if (b < C::kVBlocks) {
+    const int kb = b / (D / 4), db = b % (D / 4);
+    if (C::kVBlocks % C::kThreads == 0 || b < C::kVBlocks) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.v[i][r] = bload64(rv, (uint32_t)((j0 + 4 * kb + r) * D + 4 * db) * 2u);
+    }
+  }
+}
+
+template <int D, int BN>
+__device__ __forceinline__ void store_v_tile(const VStage<D, BN>& st, __bf16* Vts, int tid) {
+  using C = FwdCfg<D, BN>;
+#pragma unroll
+  for (int i = 0; i < C::kVPerThread; ++i) {
+    const int b = tid + i * C::kThreads;
+    if (C::kVBlocks % C::kThreads == 0 || b < C::kVBlocks) {
       const int kb = b / (D / 4), db = b % (D / 4);
       const int slot = vt_key_slot(4 * kb);
       // 4 keys x 4 features in, 4 features x 4 keys out.
       const u32x2* r = st.v[i];
-      u32x2 o0 = {pack_lo16(r[0][0], r[1][0]), pack_lo16(r[2][0], r[3][0])};
-      u32x2 o1 = {pack_hi16(r[0][0], r[1][0]), pack_hi16(r[2][0], r[3][0])};
-      u32x2 o2 = {pack_lo16(r[0][1], r[1][1]), pack_lo16(r[2][1], r[3][1])};
-      u32x2 o3 = {pack_hi16(r[0][1], r[1][1]), pack_hi16(r[2][1], r[3][1])};
+      const u32x2 o0 = {pack_lo16(r[0][0], r[1][0]), pack_lo16(r[2][0], r[3][0])};
+      const u32x2 o1 = {pack_hi16(r[0][0], r[1][0]), pack_hi16(r[2][0], r[3][0])};
+      const u32x2 o2 = {pack_lo16(r[0][1], r[1][1]), pack_lo16(r[2][1], r[3][1])};
+      const u32x2 o3 = {pack_hi16(r[0][1], r[1][1]), pack_hi16(r[2][1], r[3][1])};
       __bf16* base = Vts + (4 * db) * C::kVPitch + slot;
       *(u32x2*)(base + 0 * C::kVPitch) = o0;
       *(u32x2*)(base + 1 * C::kVPitch) = o1;
@@ -117,6 +150,145 @@ __device__ __forceinline__ void fwd_store_tile(const FwdStage<D, BN>& st, __bf16
       *(u32x2*)(base + 3 * C::kVPitch) = o3;
     }
   }
+}
+
+// S^T = K Q^T for one tile: BN keys x this wave's 32 queries.  The k-steps
+// run outermost so the BN/32 accumulator chains interleave.
+template <int D, int BN>
+__device__ __forceinline__ void score_tile(f32x16 (&s)[BN / 32], const __bf16* Ks, const bf16x8 (&qb)[D / 16],
+                                          int lc, int lg) {
+  using C = FwdCfg<D, BN>;
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
+  const __bf16* krow = Ks + lc * C::kKPitch + 8 * lg;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < BN / 32; ++mb) {
+      const bf16x8 a = *(const bf16x8*)(krow + 32 * mb * C::kKPitch + 16 * ks);
+      s[mb] = mfma32(a, qb[ks], s[mb]);
+    }
+}
+
+// Keys past the end, and on the diagonal keys after the query, to -inf.
+template <int BN>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[BN / 32], int j0, int qlim, int lg) {
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + 32 * mb + 8 * (r >> 2) + 4 * lg + (r & 3);
+      if (key > qlim) s[mb][r] = -INFINITY;
+    }
+}
+
+// Online-softmax step for one tile of scores (this lane's query column),
+// first half: raise the running max when the tile exceeds it by more than
+// kMaxSlack, rescaling O and l (rare after the first tile).
+template <int D, int BN>
+__device__ __forceinline__ void softmax_max(const f32x16 (&s)[BN / 32], float& m_run, float& l_run,
+                                            f32x16 (&oacc)[D / 32], float scale_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  mx = max_with_lane_xor32(mx) * scale_log2;
+  if (__ballot(mx > m_run + kMaxSlack)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+  }
+}
+
+// Second half: P = exp2(s * scale * log2 e - m) packed to bf16 B operands,
+// l += sum P.  Rows whose keys are all masked so far keep m = -inf; 0 is
+// used instead so exp2 gives 0 rather than NaN.
+template <int BN>
+__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[BN / 32], bf16x8 (&pb)[BN / 16], float m_run,
+                                            float& l_run, float scale_log2) {
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  float rowsum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e], scale_log2, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e + 1], scale_log2, -m_use));
+        rowsum += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pb[2 * mb + h] = __builtin_bit_cast(bf16x8, ((u32x4){w[0], w[1], w[2], w[3]}));
+    }
+  l_run += rowsum;
+}
+
+// O^T += V^T P^T for one tile.
+template <int D, int BN>
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vts,
+                                        int lc, int lg) {
+  using C = FwdCfg<D, BN>;
+  const __bf16* vrow = Vts + lc * C::kVPitch + 8 * lg;
+#pragma unroll
+  for (int c = 0; c < BN / 16; ++c)
+#pragma unroll
+    for (int dm = 0; dm < D / 32; ++dm) {
+      const bf16x8 a = *(const bf16x8*)(vrow + 32 * dm * C::kVPitch + 16 * c);
+      oacc[dm] = mfma32(a, pb[c], oacc[dm]);
+    }
+}
+
+template <int D, int BN, bool CAUSAL>
+struct FwdState {
+  const __bf16* Kbuf[2];
+  __bf16* Kw[2];
+  const __bf16* Vbuf[2];
+  __bf16* Vw[2];
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int N, num_kt, q_wave0, q_idx, tid, lc, lg;
+  float scale_log2;
+};
+
+// One key tile: prefetch K(t+2) and V(t+1) into registers, turn S(t) into
+// P while issuing S(t+1) = K(t+1) Q^T, accumulate P V(t), then publish the
+// prefetched tiles to LDS and synchronise.
+template <int D, int BN, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile_step(const FwdState<D, BN, CAUSAL>& g, int t, f32x16 (&sc)[BN / 32],
+                                              f32x16 (&sn)[BN / 32], const bf16x8 (&qb)[D / 16],
+                                              f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                              KStage<D, BN>& stk, VStage<D, BN>& stv) {
+  const int j0 = t * BN;
+  const bool has_next = t + 1 < g.num_kt;
+  const bool has_next2 = t + 2 < g.num_kt;
+  if (has_next2) load_k_tile<D, BN>(stk, g.rk, j0 + 2 * BN, g.tid);
+  if (has_next) load_v_tile<D, BN>(stv, g.rv, j0 + BN, g.tid);
+  const bool live = !CAUSAL || j0 <= g.q_wave0 + 31;
+  if (live) {
+    const bool need_mask = (j0 + BN > g.N) || (CAUSAL && j0 + BN - 1 > g.q_wave0);
+    if (need_mask) mask_tile<BN>(sc, j0, CAUSAL ? min(g.q_idx, g.N - 1) : g.N - 1, g.lg);
+    softmax_max<D, BN>(sc, m_run, l_run, oacc, g.scale_log2);
+    // One straight-line block: the next tile's score MFMAs, this tile's
+    // exponentials, and this tile's P V MFMAs, for the scheduler to
+    // interleave.  S(t+1) is formed even when no live tile t+1 follows (the
+    // last tile, or the last live tile of a wave on the causal diagonal):
+    // one wasted tile of MFMAs per wave buys a branch-free block; the stale
+    // result is never read.
+    bf16x8 pb[BN / 16];
+    score_tile<D, BN>(sn, g.Kbuf[(t + 1) & 1], qb, g.lc, g.lg);
+    softmax_exp<BN>(sc, pb, m_run, l_run, g.scale_log2);
+    pv_tile<D, BN>(oacc, pb, g.Vbuf[t & 1], g.lc, g.lg);
+  }
+  // (A wave that is not live for tile t is not live for t+1 either: keys
+  // only grow, so S(t+1) is never needed when tile t is skipped.)
+  if (has_next2) store_k_tile<D, BN>(stk, g.Kw[t & 1], g.tid);
+  if (has_next) store_v_tile<D, BN>(stv, g.Vw[(t + 1) & 1], g.tid);
+  __syncthreads();
 }
 
 template <int D, int BN, bool CAUSAL>
@@ -127,148 +299,92 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using C = FwdCfg<D, BN>;
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int lc = lane & 31;     // lane column: query within the wave
-  const int lg = lane >> 5;     // lane half
+  FwdState<D, BN, CAUSAL> g;
+  g.tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // uniform per wave
+  const int lane = g.tid & 63;
+  g.lc = lane & 31;     // lane column: query within the wave
+  g.lg = lane >> 5;     // lane half
 
   const int bid = blockIdx.x;
   const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
   const int bh = bid % BH;
   const size_t head_off = (size_t)bh * N * D;
-  const __bf16* Qh = Q + head_off;
-  const __bf16* Kh = K + head_off;
-  const __bf16* Vh = V + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + head_off, head_bytes);
+  g.rk = head_rsrc(K + head_off, head_bytes);
+  g.rv = head_rsrc(V + head_off, head_bytes);
+  g.N = N;
+  g.scale_log2 = scale_log2;
+  g.q_wave0 = qt * C::BM + wave * 32;
+  g.q_idx = g.q_wave0 + g.lc;
+  g.Kw[0] = smem;
+  g.Kw[1] = smem + C::kKTile;
+  g.Vw[0] = smem + 2 * C::kKTile;
+  g.Vw[1] = smem + 2 * C::kKTile + C::kVTile;
+  for (int i = 0; i < 2; ++i) {
+    g.Kbuf[i] = g.Kw[i];
+    g.Vbuf[i] = g.Vw[i];
+  }
 
-  const int q_wave0 = qt * C::BM + wave * 32;
-  const int q_idx = q_wave0 + lc;
-
-  // Q^T as MFMA B operand: lane holds Q[q][16 ks + 8 lg .. +7].
+  // Q^T as MFMA B operand: lane holds Q[q][16 ks + 8 lg .. +7] (zeros past N).
   bf16x8 qb[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (q_idx < N) val = *(const u32x4*)(Qh + (size_t)q_idx * D + 16 * ks + 8 * lg);
-    qb[ks] = __builtin_bit_cast(bf16x8, val);
-  }
+  for (int ks = 0; ks < D / 16; ++ks)
+    qb[ks] = __builtin_bit_cast(bf16x8, bload128(rq, (uint32_t)(g.q_idx * D + 16 * ks + 8 * g.lg) * 2u));
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = (f32x16){};
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s
+  float m_run = -INFINITY;   // running reference max of scale*log2(e)*s
   float l_run = 0.f;         // this lane's share of the running sum
 
   const int q_tile_end = min(N, (qt + 1) * C::BM);
   const int key_end = CAUSAL ? q_tile_end : N;
-  const int num_kt = (key_end + BN - 1) / BN;
+  g.num_kt = (key_end + BN - 1) / BN;
 
-  FwdStage<D, BN> st;
-  fwd_load_tile<D, BN>(st, Kh, Vh, 0, N, tid);
-  fwd_store_tile<D, BN>(st, smem, smem + C::kKTile, tid);
-
-  for (int t = 0; t < num_kt; ++t) {
-    const int j0 = t * BN;
-    if (t + 1 < num_kt) fwd_load_tile<D, BN>(st, Kh, Vh, j0 + BN, N, tid);
-    __syncthreads();
-    const __bf16* Ks = smem + (t & 1) * C::kStage;
-    const __bf16* Vts = Ks + C::kKTile;
-
-    const bool wave_live = !CAUSAL || j0 <= q_wave0 + 31;
-    if (wave_live) {
-      // S^T = K Q^T for this tile: BN keys x 32 queries.
-      f32x16 s[BN / 32];
-#pragma unroll
-      for (int mb = 0; mb < BN / 32; ++mb) {
-        f32x16 acc = (f32x16){};
-        const __bf16* krow = Ks + (32 * mb + lc) * C::kKPitch + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          bf16x8 a = *(const bf16x8*)(krow + 16 * ks);
-          acc = mfma32(a, qb[ks], acc);
-        }
-        s[mb] = acc;
-      }
-      // Mask keys past the end and, on the diagonal, keys after the query.
-      const bool need_mask = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q_wave0);
-      if (need_mask) {
-        const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
-#pragma unroll
-        for (int mb = 0; mb < BN / 32; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * mb + 8 * (r >> 2) + 4 * lg + (r & 3);
-            if (key > qlim) s[mb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < BN / 32; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      mx = max_with_lane_xor32(mx);
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-
-      // P = exp2(s * scale * log2(e) - m), packed to bf16 as the B operand.
-      bf16x8 pb[BN / 16];
-      float rowsum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < BN / 32; ++mb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e], scale_log2, -m_use));
-            const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e + 1], scale_log2, -m_use));
-            rowsum += p0 + p1;
-            w[e] = pack_bf16x2(p0, p1);
-          }
-          u32x4 wv = {w[0], w[1], w[2], w[3]};
-          pb[2 * mb + h] = __builtin_bit_cast(bf16x8, wv);
-        }
-      }
-      l_run = l_run * alpha + rowsum;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      }
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int c = 0; c < BN / 16; ++c) {
-#pragma unroll
-        for (int dm = 0; dm < D / 32; ++dm) {
-          bf16x8 a = *(const bf16x8*)(Vts + (32 * dm + lc) * C::kVPitch + 16 * c + 8 * lg);
-          oacc[dm] = mfma32(a, pb[c], oacc[dm]);
-        }
-      }
+  // Prologue: K(0), V(0), K(1) into LDS; S(0).
+  {
+    KStage<D, BN> k0;
+    VStage<D, BN> v0;
+    load_k_tile<D, BN>(k0, g.rk, 0, g.tid);
+    load_v_tile<D, BN>(v0, g.rv, 0, g.tid);
+    store_k_tile<D, BN>(k0, g.Kw[0], g.tid);
+    store_v_tile<D, BN>(v0, g.Vw[0], g.tid);
+    if (g.num_kt > 1) {
+      load_k_tile<D, BN>(k0, g.rk, BN, g.tid);
+      store_k_tile<D, BN>(k0, g.Kw[1], g.tid);
     }
-    if (t + 1 < num_kt) {
-      __bf16* Kn = smem + ((t + 1) & 1) * C::kStage;
-      fwd_store_tile<D, BN>(st, Kn, Kn + C::kKTile, tid);
-    }
+  }
+  __syncthreads();
+  f32x16 sa[BN / 32], sb[BN / 32];
+  score_tile<D, BN>(sa, g.Kbuf[0], qb, g.lc, g.lg);
+
+  KStage<D, BN> stk;
+  VStage<D, BN> stv;
+  for (int t = 0; t < g.num_kt; t += 2) {
+    fwd_tile_step<D, BN, CAUSAL>(g, t, sa, sb, qb, oacc, m_run, l_run, stk, stv);
+    if (t + 1 < g.num_kt) fwd_tile_step<D, BN, CAUSAL>(g, t + 1, sb, sa, qb, oacc, m_run, l_run, stk, stv);
   }
 
   // Epilogue: O / l rounded to bf16, and LSE = m + ln l (natural log).
   const float l_tot = sum_with_lane_xor32(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_idx < N) {
-    __bf16* orow = O + head_off + (size_t)q_idx * D;
+  if (g.q_idx < N) {
+    __bf16* orow = O + head_off + (size_t)g.q_idx * D;
 #pragma unroll
     for (int dm = 0; dm < D / 32; ++dm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * inv_l, oacc[dm][4 * i + 1] * inv_l),
                    pack_bf16x2(oacc[dm][4 * i + 2] * inv_l, oacc[dm][4 * i + 3] * inv_l)};
-        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * lg) = w;
+        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * g.lg) = w;
       }
-    if (LSE != nullptr && lg == 0)
-      LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+    if (LSE != nullptr && g.lg == 0)
+      LSE[(size_t)bh * N + g.q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // fp32 forward: float32 storage and arithmetic throughout (no bf16 rounding
@@ -391,14 +507,8 @@ hipError_t launch_fwd(const FwdArgs& a) {
     return a.causal ? launch_f32<128, true>(a) : launch_f32<128, false>(a);
   }
   const int bn = a.block_n == 0 ? 64 : a.block_n;
-  if (a.d == 64) {
-    if (bn == 32) return launch_bf16_bn<64, 32>(a);
-    if (bn == 64) return launch_bf16_bn<64, 64>(a);
-    return launch_bf16_bn<64, 128>(a);
-  }
-  if (bn == 32) return launch_bf16_bn<128, 32>(a);
-  if (bn == 64) return launch_bf16_bn<128, 64>(a);
-  return launch_bf16_bn<128, 128>(a);
+  if (a.d == 64) return bn == 32 ? launch_bf16_bn<64, 32>(a) : launch_bf16_bn<64, 64>(a);
+  return bn == 32 ? launch_bf16_bn<128, 32>(a) : launch_bf16_bn<128, 64>(a);
 }
 
 }  // namespace fa

@@ -85,6 +85,7 @@ def fwd(**kw):
     (dict(d=256), binding.FA_ERR_UNSUPPORTED),
     (dict(dtype=7), binding.FA_ERR_UNSUPPORTED),
     (dict(block_n=48), binding.FA_ERR_UNSUPPORTED),
+    (dict(block_n=128), binding.FA_ERR_UNSUPPORTED),
     (dict(block_n=64, dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
     (dict(lse=MISALIGNED), binding.FA_ERR_INVALID_ARG),
 ])

@@ -78,7 +78,7 @@ def test_block_size_never_changes_answer(d, causal):
     shape = (1, 3, 390, d)
     inp = wl.make_inputs(shape, 3000 + d, "bf16")
     outs = []
-    for bn in (32, 64, 128):
+    for bn in (32, 64):
         announce(f"fwd bf16 shape={shape} causal={causal} block_n={bn}")
         o, lse = run_fwd(inp, "bf16", causal, block_n=bn)
         check_heads(inp, "bf16", causal, o, lse, [(0, h) for h in range(3)])
