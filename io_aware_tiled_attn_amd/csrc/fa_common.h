@@ -63,4 +63,50 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed operand reads from a row-major LDS matrix M with ds_read_b64_tr_b16.
+// That instruction hands lane j of each 16-lane group element j % 4 of the
+// 8-byte word read by lane 4 e + j / 4 of the group, for e = 0..3; so when
+// lane s of a group reads row s / 4 at column 4 (s % 4) of a 4 x 16 block,
+// lane j receives the 4 rows of column j.  Two such reads give the 8 k-values
+// of an MFMA A or B operand whose k-dimension runs down M's rows.
+//
+// tr_lane_off is the lane-dependent part of the element offset: lane l reads
+// column l % 32 of its block; lane half g = l / 32 starts `half_rows` rows
+// further down.  Callers add compile-time row/column offsets.
+__device__ __forceinline__ int tr_lane_off(int lane, int pitch, int half_rows) {
+  const int s = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
+  return (half_rows * g + (s >> 2)) * pitch + 16 * G + 4 * (s & 3);
+}
+
+// p already includes tr_lane_off; lo and hi are element offsets of the two
+// 4-row groups (slots 0..3 and 4..7 of the result).
+__device__ __forceinline__ bf16x8 lds_tr_pair(const __bf16* p, int lo, int hi) {
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Buffer descriptor over `bytes` bytes at p (raw, 32-bit data format):
+// loads at offsets >= bytes return 0 and atomics there are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ float bload32f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void batomic_add(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)off, 0, 0);
+}
+
 }  // namespace fa

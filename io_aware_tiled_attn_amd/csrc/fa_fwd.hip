@@ -19,10 +19,12 @@
 //     scores, so the matrix cores and the vector ALU overlap inside a wave
 //     as well as across the two waves sharing a SIMD.  Double buffers for K
 //     and for V with one barrier per tile.
-//   * K is stored row-major with padding; V is stored transposed
-//     (V^T[d][key]) with the keys of each 16-key group reordered so that the
-//     A operand of O^T += V^T P^T is one 16-byte LDS read per lane and
-//     matches the key order the S^T accumulator leaves in each lane.
+//   * K and V are stored row-major with padding.  The A operand of
+//     O^T += V^T P^T (V transposed) is read with ds_read_b64_tr_b16, which
+//     hands each lane four consecutive keys of one feature column; the two
+//     reads per operand take the key order the S^T accumulator leaves in each
+//     lane.  V's row pitch (d + 32 elements) puts the four rows read by each
+//     16-lane group, and the two groups of a half-wave, on disjoint banks.
 //   * P is rounded to bf16 (RNE) and fed back as the B operand directly from
 //     the accumulator registers; O^T accumulates in fp32.
 //   * The running max is raised only when a tile's max exceeds it by more
@@ -48,106 +50,46 @@ struct FwdCfg {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int BM = kWaves * 32;
   static constexpr int kKPitch = D + 8;    // bf16 elements per K row in LDS
-  static constexpr int kVPitch = BN + 8;   // bf16 elements per V^T row in LDS
+  static constexpr int kVPitch = D + 32;   // bf16 elements per V row in LDS
   static constexpr int kKTile = BN * kKPitch;
-  static constexpr int kVTile = D * kVPitch;
-  // LDS: K buffer 0 | K buffer 1 | V^T buffer 0 | V^T buffer 1
+  static constexpr int kVTile = BN * kVPitch;
+  // LDS: K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1
   static constexpr int kLdsBytes = 2 * (kKTile + kVTile) * 2;
-  static constexpr int kKChunks = BN * D / 8;             // 16-byte K chunks
-  static constexpr int kKPerThread = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVBlocks = (BN / 4) * (D / 4);     // 4x4 V blocks
-  static constexpr int kVPerThread = (kVBlocks + kThreads - 1) / kThreads;
+  static constexpr int kChunks = BN * D / 8;              // 16-byte chunks per tile
+  static constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
 };
 
-// Position of key k (0 <= k < BN) inside its LDS row of V^T: bits 2 and 3
-// swapped, so keys {4g..4g+3, 8+4g..8+4g+3} of each 16-key group are
-// adjacent for lane half g.
-__device__ __forceinline__ int vt_key_slot(int k) {
-  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
-// Buffer descriptor over `bytes` bytes at p (raw, 32-bit data format):
-// loads at offsets >= bytes return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-
 template <int D, int BN>
-struct KStage {
-  u32x4 k[FwdCfg<D, BN>::kKPerThread];
-};
-template <int D, int BN>
-struct VStage {
-  u32x2 v[FwdCfg<D, BN>::kVPerThread][4];
+struct TileStage {
+  u32x4 c[FwdCfg<D, BN>::kPerThread];
 };
 
+// Global -> registers: this thread's 16-byte chunks of a BN x D tile (rows
+// past the head's end read as zero through the buffer descriptor).
 template <int D, int BN>
-__device__ __forceinline__ void load_k_tile(KStage<D, BN>& st, __amdgpu_buffer_rsrc_t rk, int j0, int tid) {
+__device__ __forceinline__ void load_tile(TileStage<D, BN>& st, __amdgpu_buffer_rsrc_t r, int j0, int tid) {
   using C = FwdCfg<D, BN>;
 #pragma unroll
-  for (int i = 0; i < C::kKPerThread; ++i) {
+  for (int i = 0; i < C::kPerThread; ++i) {
     const int c = tid + i * C::kThreads;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    if (C::kKChunks % C::kThreads == 0 || c < C::kKChunks)
-      st.k[i] = bload128(rk, (uint32_t)((j0 + row) * D + col) * 2u);
+    if (C::kChunks % C::kThreads == 0 || c < C::kChunks)
+      st.c[i] = bload128(r, (uint32_t)((j0 + row) * D + col) * 2u);
   }
 }
 
-template <int D, int BN>
-__device__ __forceinline__ void store_k_tile(const KStage<D, BN>& st, __bf16* Ks, int tid) {
+// Registers -> LDS, row-major with `pitch` elements per row.
+template <int D, int BN, int PITCH>
+__device__ __forceinline__ void store_tile(const TileStage<D, BN>& st, __bf16* S, int tid) {
   using C = FwdCfg<D, BN>;
 #pragma unroll
-  for (int i = 0; i < C::kKPerThread; ++i) {
+  for (int i = 0; i < C::kPerThread; ++i) {
     const int c = tid + i * C::kThreads;
-    if (C::kKChunks % C::kThreads == 0 || c < C::kKChunks) {
+    if (C::kChunks % C::kThreads == 0 || c < C::kChunks) {
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)(Ks + row * C::kKPitch + col) = st.k[i];
-    }
-  }
-}
-
-template <int D, int BN>
-__device__ __forceinline__ void load_v_tile(VStage<D, BN>& st, __amdgpu_buffer_rsrc_t rv, int j0, int tid) {
-  using C = FwdCfg<D, BN>;
-#pragma unroll
-  for (int i = 0; i < C::kVPerThread; ++i) {
-    const int b = tid + i * C::kThreads;
-    const int kb = b / (D / 4), db = b % (D / 4);
-    if (C::kVBlocks % C::kThreads == 0 || b < C::kVBlocks) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.v[i][r] = bload64(rv, (uint32_t)((j0 + 4 * kb + r) * D + 4 * db) * 2u);
-    }
-  }
-}
-
-template <int D, int BN>
-__device__ __forceinline__ void store_v_tile(const VStage<D, BN>& st, __bf16* Vts, int tid) {
-  using C = FwdCfg<D, BN>;
-#pragma unroll
-  for (int i = 0; i < C::kVPerThread; ++i) {
-    const int b = tid + i * C::kThreads;
-    if (C::kVBlocks % C::kThreads == 0 || b < C::kVBlocks) {
-      const int kb = b / (D / 4), db = b % (D / 4);
-      const int slot = vt_key_slot(4 * kb);
-      // 4 keys x 4 features in, 4 features x 4 keys out.
-      const u32x2* r = st.v[i];
-      const u32x2 o0 = {pack_lo16(r[0][0], r[1][0]), pack_lo16(r[2][0], r[3][0])};
-      const u32x2 o1 = {pack_hi16(r[0][0], r[1][0]), pack_hi16(r[2][0], r[3][0])};
-      const u32x2 o2 = {pack_lo16(r[0][1], r[1][1]), pack_lo16(r[2][1], r[3][1])};
-      const u32x2 o3 = {pack_hi16(r[0][1], r[1][1]), pack_hi16(r[2][1], r[3][1])};
-      __bf16* base = Vts + (4 * db) * C::kVPitch + slot;
-      *(u32x2*)(base + 0 * C::kVPitch) = o0;
-      *(u32x2*)(base + 1 * C::kVPitch) = o1;
-      *(u32x2*)(base + 2 * C::kVPitch) = o2;
-      *(u32x2*)(base + 3 * C::kVPitch) = o3;
+      *(u32x4*)(S + row * PITCH + col) = st.c[i];
     }
   }
 }
@@ -229,17 +171,19 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[BN / 32], bf16x8 (
   l_run += rowsum;
 }
 
-// O^T += V^T P^T for one tile.
+// O^T += V^T P^T for one tile.  V^T's operand for k-step c holds, in lane
+// half g, keys 16c + 4g + 0..3 and 16c + 8 + 4g + 0..3: the keys P's
+// accumulator layout leaves in that lane half.
 template <int D, int BN>
-__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vts,
-                                        int lc, int lg) {
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vs,
+                                        int v_lane_off) {
   using C = FwdCfg<D, BN>;
-  const __bf16* vrow = Vts + lc * C::kVPitch + 8 * lg;
+  const __bf16* vp = Vs + v_lane_off;
 #pragma unroll
   for (int c = 0; c < BN / 16; ++c)
 #pragma unroll
     for (int dm = 0; dm < D / 32; ++dm) {
-      const bf16x8 a = *(const bf16x8*)(vrow + 32 * dm * C::kVPitch + 16 * c);
+      const bf16x8 a = lds_tr_pair(vp, (16 * c) * C::kVPitch + 32 * dm, (16 * c + 8) * C::kVPitch + 32 * dm);
       oacc[dm] = mfma32(a, pb[c], oacc[dm]);
     }
 }
@@ -251,7 +195,7 @@ struct FwdState {
   const __bf16* Vbuf[2];
   __bf16* Vw[2];
   __amdgpu_buffer_rsrc_t rk, rv;
-  int N, num_kt, q_wave0, q_idx, tid, lc, lg;
+  int N, num_kt, q_wave0, q_idx, tid, v_lane_off, lc, lg;
   float scale_log2;
 };
 
@@ -262,12 +206,13 @@ template <int D, int BN, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile_step(const FwdState<D, BN, CAUSAL>& g, int t, f32x16 (&sc)[BN / 32],
                                               f32x16 (&sn)[BN / 32], const bf16x8 (&qb)[D / 16],
                                               f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
-                                              KStage<D, BN>& stk, VStage<D, BN>& stv) {
+                                              TileStage<D, BN>& stk, TileStage<D, BN>& stv) {
+  using C = FwdCfg<D, BN>;
   const int j0 = t * BN;
   const bool has_next = t + 1 < g.num_kt;
   const bool has_next2 = t + 2 < g.num_kt;
-  if (has_next2) load_k_tile<D, BN>(stk, g.rk, j0 + 2 * BN, g.tid);
-  if (has_next) load_v_tile<D, BN>(stv, g.rv, j0 + BN, g.tid);
+  if (has_next2) load_tile<D, BN>(stk, g.rk, j0 + 2 * BN, g.tid);
+  if (has_next) load_tile<D, BN>(stv, g.rv, j0 + BN, g.tid);
   const bool live = !CAUSAL || j0 <= g.q_wave0 + 31;
   if (live) {
     const bool need_mask = (j0 + BN > g.N) || (CAUSAL && j0 + BN - 1 > g.q_wave0);
@@ -282,12 +227,12 @@ __device__ __forceinline__ void fwd_tile_step(const FwdState<D, BN, CAUSAL>& g, 
     bf16x8 pb[BN / 16];
     score_tile<D, BN>(sn, g.Kbuf[(t + 1) & 1], qb, g.lc, g.lg);
     softmax_exp<BN>(sc, pb, m_run, l_run, g.scale_log2);
-    pv_tile<D, BN>(oacc, pb, g.Vbuf[t & 1], g.lc, g.lg);
+    pv_tile<D, BN>(oacc, pb, g.Vbuf[t & 1], g.v_lane_off);
   }
   // (A wave that is not live for tile t is not live for t+1 either: keys
   // only grow, so S(t+1) is never needed when tile t is skipped.)
-  if (has_next2) store_k_tile<D, BN>(stk, g.Kw[t & 1], g.tid);
-  if (has_next) store_v_tile<D, BN>(stv, g.Vw[(t + 1) & 1], g.tid);
+  if (has_next2) store_tile<D, BN, C::kKPitch>(stk, g.Kw[t & 1], g.tid);
+  if (has_next) store_tile<D, BN, C::kVPitch>(stv, g.Vw[(t + 1) & 1], g.tid);
   __syncthreads();
 }
 
@@ -303,6 +248,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   g.tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // uniform per wave
   const int lane = g.tid & 63;
+  g.v_lane_off = tr_lane_off(lane, C::kVPitch, 4);
   g.lc = lane & 31;     // lane column: query within the wave
   g.lg = lane >> 5;     // lane half
 
@@ -311,9 +257,9 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int bh = bid % BH;
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + head_off, head_bytes);
-  g.rk = head_rsrc(K + head_off, head_bytes);
-  g.rv = head_rsrc(V + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
+  g.rk = make_rsrc(K + head_off, head_bytes);
+  g.rv = make_rsrc(V + head_off, head_bytes);
   g.N = N;
   g.scale_log2 = scale_log2;
   g.q_wave0 = qt * C::BM + wave * 32;
@@ -345,23 +291,21 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // Prologue: K(0), V(0), K(1) into LDS; S(0).
   {
-    KStage<D, BN> k0;
-    VStage<D, BN> v0;
-    load_k_tile<D, BN>(k0, g.rk, 0, g.tid);
-    load_v_tile<D, BN>(v0, g.rv, 0, g.tid);
-    store_k_tile<D, BN>(k0, g.Kw[0], g.tid);
-    store_v_tile<D, BN>(v0, g.Vw[0], g.tid);
+    TileStage<D, BN> k0, v0;
+    load_tile<D, BN>(k0, g.rk, 0, g.tid);
+    load_tile<D, BN>(v0, g.rv, 0, g.tid);
+    store_tile<D, BN, C::kKPitch>(k0, g.Kw[0], g.tid);
+    store_tile<D, BN, C::kVPitch>(v0, g.Vw[0], g.tid);
     if (g.num_kt > 1) {
-      load_k_tile<D, BN>(k0, g.rk, BN, g.tid);
-      store_k_tile<D, BN>(k0, g.Kw[1], g.tid);
+      load_tile<D, BN>(k0, g.rk, BN, g.tid);
+      store_tile<D, BN, C::kKPitch>(k0, g.Kw[1], g.tid);
     }
   }
   __syncthreads();
   f32x16 sa[BN / 32], sb[BN / 32];
   score_tile<D, BN>(sa, g.Kbuf[0], qb, g.lc, g.lg);
 
-  KStage<D, BN> stk;
-  VStage<D, BN> stv;
+  TileStage<D, BN> stk, stv;
   for (int t = 0; t < g.num_kt; t += 2) {
     fwd_tile_step<D, BN, CAUSAL>(g, t, sa, sb, qb, oacc, m_run, l_run, stk, stv);
     if (t + 1 < g.num_kt) fwd_tile_step<D, BN, CAUSAL>(g, t + 1, sb, sa, qb, oacc, m_run, l_run, stk, stv);
