@@ -16,11 +16,11 @@
 //      wave keeps its 32 keys' K and V rows in registers (the B operands of
 //      S = Q K^T and dP = dO V^T, so each lane owns one key column of the
 //      32x32 accumulators) and accumulates dK^T and dV^T for them in fp32.
-//      The workgroup walks 32-row query tiles (Q, dO, LSE, D staged through
-//      LDS, double buffered); dV^T += dO^T P and dK^T += Q^T dS take their
+//      The workgroup walks 64-row query tiles (Q, dO, LSE, D staged through
+//      LDS, double buffered), two 32-row blocks per wave and step; dV^T += dO^T P and dK^T += Q^T dS take their
 //      transposed A operands with ds_read_b64_tr_b16.  dS goes through LDS
 //      once (as dS^T) so that dQ = dS K can be formed for the tile, and each
-//      wave adds its 32 x 32 block of dQ to the fp32 accumulator with
+//      wave adds its 32 x 32 blocks of dQ to the fp32 accumulator with
 //      hardware float atomics.  P and dS enter the dV, dK and dQ products as
 //      two bf16 terms each (rounded value + residual): one bf16 term alone
 //      leaves a relative error of up to 2^-9 per element, which at N = 4096
@@ -30,9 +30,6 @@
 #include "fa_internal.h"
 
 namespace fa {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ---------------------------------------------------------------------------
 // 1. D_i = sum_c dO_ic O_ic; zero the dQ accumulator.
@@ -68,8 +65,9 @@ template <int D>
 struct BwdCfg {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 256;
-  static constexpr int BN = 128;                 // keys per workgroup
-  static constexpr int BM = 32;                  // queries per step
+  static constexpr int BN = 128;                 // keys per workgroup (32 per wave)
+  static constexpr int BM = 64;                  // queries per step
+  static constexpr int QB = BM / 32;             // 32-query blocks per step
   static constexpr int kRowPitch = D + 8;        // Q / dO tile rows in LDS
   static constexpr int kKtPitch = BN + 8;        // K^T rows in LDS
   static constexpr int kDsPitch = BM + 8;        // dS^T rows in LDS
@@ -81,28 +79,14 @@ struct BwdCfg {
   static constexpr int kLdsBytes = kKtBytes + 2 * kStageBytes + kDsBytes;
   static constexpr int kChunks = BM * D / 8;     // 16-byte chunks per Q tile
   static constexpr int kChunksPerThread = kChunks / kThreads;
+  // dQ blocks (32 queries x 32 features) per step, shared out over the waves.
+  static constexpr int kDqBlocks = QB * (D / 32);
+  static constexpr int kDqPerWave = kDqBlocks / kWaves;
   static_assert(kChunks % kThreads == 0, "tile staging");
+  static_assert(kDqBlocks % kWaves == 0, "dQ work split");
   static_assert(kThreads == 256, "kernel launch bounds assume 256 threads");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
-
-// 8 bf16 taken down the rows of a row-major LDS matrix: lane l receives
-// M[r_lo + 0..3][col0 + l % 32] as slots 0..3 and M[r_hi + 0..3][col0 + l % 32]
-// as slots 4..7 (r_lo, r_hi may differ between the two lane halves).
-// ds_read_b64_tr_b16 hands lane j of each 16-lane group element j % 4 of the
-// 8-byte word read by lane 4 e + j / 4 of that group, for e = 0..3; so lane s
-// of the group reads row (s / 4) at column 4 (s % 4) of its 4 x 16 block.
-__device__ __forceinline__ bf16x8 lds_read_down(const __bf16* M, int pitch, int col0, int r_lo, int r_hi,
-                                                int lane) {
-  const int s = lane & 15, G = lane >> 4;
-  const int col = col0 + 16 * (G & 1) + 4 * (s & 3);
-  const __bf16* p0 = M + (r_lo + (s >> 2)) * pitch + col;
-  const __bf16* p1 = M + (r_hi + (s >> 2)) * pitch + col;
-  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, r);
-}
 
 template <int D>
 struct BwdStage {
@@ -112,29 +96,29 @@ struct BwdStage {
   float dlt;    // D for one row (threads BM..2BM-1)
 };
 
+// Per-head buffer descriptors: rows past N read as zero; dQ atomics past N
+// are dropped.
+struct BwdHead {
+  __amdgpu_buffer_rsrc_t q, k, v, g, lse, dlt, dq;
+};
+
 template <int D>
-__device__ __forceinline__ void bwd_load_stage(BwdStage<D>& st, const __bf16* Qh, const __bf16* dOh,
-                                               const float* lse_h, const float* dlt_h, int q0, int N, int tid) {
+__device__ __forceinline__ void bwd_load_stage(BwdStage<D>& st, const BwdHead& h, int q0, int N, int tid) {
   using C = BwdCfg<D>;
 #pragma unroll
   for (int i = 0; i < C::kChunksPerThread; ++i) {
     const int c = tid + i * C::kThreads;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    const int q = q0 + row;
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (q < N) {
-      a = *(const u32x4*)(Qh + (size_t)q * D + col);
-      b = *(const u32x4*)(dOh + (size_t)q * D + col);
-    }
-    st.q[i] = a;
-    st.g[i] = b;
+    const uint32_t off = (uint32_t)((q0 + row) * D + col) * 2u;
+    st.q[i] = bload128(h.q, off);
+    st.g[i] = bload128(h.g, off);
   }
+  // LSE * log2(e) (+inf past N, so P = 0 there) and D (0 past N).
   if (tid < C::BM) {
     const int q = q0 + tid;
-    st.lse2 = q < N ? lse_h[q] * kLog2e : INFINITY;
+    st.lse2 = q < N ? bload32f(h.lse, (uint32_t)q * 4u) * kLog2e : INFINITY;
   } else if (tid < 2 * C::BM) {
-    const int q = q0 + tid - C::BM;
-    st.dlt = q < N ? dlt_h[q] : 0.f;
+    st.dlt = bload32f(h.dlt, (uint32_t)(q0 + tid - C::BM) * 4u);
   }
 }
 
@@ -156,6 +140,12 @@ __device__ __forceinline__ void bwd_store_stage(const BwdStage<D>& st, char* sta
   else if (tid < 2 * C::BM) Ds[tid - C::BM] = st.dlt;
 }
 
+// B operands (k = query, in the accumulator's lane order) for the P and dS
+// terms of one 32-query block: rounded value and rounded residual.
+struct PdsOperands {
+  bf16x8 p[2], pl[2], ds[2], dsl[2];
+};
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -163,6 +153,7 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
                    float* __restrict__ dq_acc, __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH,
                    float scale, float scale_log2) {
   using C = BwdCfg<D>;
+  constexpr int QB = C::QB;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   __bf16* Kt = (__bf16*)smem_raw;                                  // [D][kKtPitch]
   char* stages = smem_raw + C::kKtBytes;
@@ -170,40 +161,44 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
   __bf16* dSt_lo = dSt + C::BN * C::kDsPitch;                      // lo term
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // uniform per wave
+  const int lane = tid & 63;
   const int lc = lane & 31, lg = lane >> 5;
   const int kt = blockIdx.x / BH;       // key tile; small kt = most query tiles
   const int bh = blockIdx.x % BH;
   const size_t head_off = (size_t)bh * N * D;
-  const __bf16* Qh = Q + head_off;
-  const __bf16* Kh = K + head_off;
-  const __bf16* Vh = V + head_off;
-  const __bf16* dOh = dO + head_off;
-  const float* lse_h = LSE + (size_t)bh * N;
-  const float* dlt_h = delta + (size_t)bh * N;
-  float* dqh = dq_acc + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  BwdHead h;
+  h.q = make_rsrc(Q + head_off, head_bytes);
+  h.k = make_rsrc(K + head_off, head_bytes);
+  h.v = make_rsrc(V + head_off, head_bytes);
+  h.g = make_rsrc(dO + head_off, head_bytes);
+  h.lse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  h.dlt = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4u);
+  h.dq = make_rsrc(dq_acc + head_off, head_bytes * 2u);
 
   const int k0 = kt * C::BN;                  // first key of the workgroup
-  const int key = k0 + wave * 32 + lc;        // this lane's key column
+  const int kw0 = k0 + wave * 32;             // first key of this wave
+  const int key = kw0 + lc;                   // this lane's key column
+  const bool key_ok = key < N;
+  // Lane parts of the LDS offsets (the rest are compile-time constants).
+  const int row_lane_off = lc * C::kRowPitch + 8 * lg;          // Q / dO rows as A operands
+  const int tr_off_p = tr_lane_off(lane, C::kRowPitch, 4);      // Q^T / dO^T, accumulator key order
+  const int tr_off_n = tr_lane_off(lane, C::kDsPitch, 8);       // dS from dS^T, natural key order
+  const int kt_lane_off = lc * C::kKtPitch + 8 * lg;            // K (from K^T) as B operand
 
   // K and V rows of this lane's key as B operands (k = feature).
   bf16x8 kb[D / 16], vb[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key < N) {
-      a = *(const u32x4*)(Kh + (size_t)key * D + 16 * ks + 8 * lg);
-      b = *(const u32x4*)(Vh + (size_t)key * D + 16 * ks + 8 * lg);
-    }
-    kb[ks] = __builtin_bit_cast(bf16x8, a);
-    vb[ks] = __builtin_bit_cast(bf16x8, b);
+    const uint32_t off = (uint32_t)(key * D + 16 * ks + 8 * lg) * 2u;
+    kb[ks] = __builtin_bit_cast(bf16x8, bload128(h.k, off));
+    vb[ks] = __builtin_bit_cast(bf16x8, bload128(h.v, off));
   }
   // K^T of the workgroup's keys in LDS for dQ = dS K.
   for (int e = tid; e < C::BN * (D / 4); e += C::kThreads) {
     const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
-    const int kk = k0 + r;
-    u32x2 val = {0u, 0u};
-    if (kk < N) val = *(const u32x2*)(Kh + (size_t)kk * D + c4);
+    const u32x2 val = bload64(h.k, (uint32_t)((k0 + r) * D + c4) * 2u);
     __bf16 tmp[4];
     *(u32x2*)tmp = val;
 #pragma unroll
@@ -222,14 +217,14 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
   const int qt_end = (N + C::BM - 1) / C::BM;
   BwdStage<D> st;
   if (qt_begin < qt_end) {
-    bwd_load_stage<D>(st, Qh, dOh, lse_h, dlt_h, qt_begin * C::BM, N, tid);
+    bwd_load_stage<D>(st, h, qt_begin * C::BM, N, tid);
     bwd_store_stage<D>(st, stages, tid);
   }
 
   for (int qt = qt_begin; qt < qt_end; ++qt) {
     const int it = qt - qt_begin;
     const int q0 = qt * C::BM;
-    if (qt + 1 < qt_end) bwd_load_stage<D>(st, Qh, dOh, lse_h, dlt_h, q0 + C::BM, N, tid);
+    if (qt + 1 < qt_end) bwd_load_stage<D>(st, h, q0 + C::BM, N, tid);
     __syncthreads();   // stage `it` visible; previous dS^T reads finished
     char* stage = stages + (it & 1) * C::kStageBytes;
     const __bf16* Qs = (const __bf16*)stage;
@@ -237,97 +232,131 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     const float* Ls = (const float*)(Gs + C::kTile);
     const float* Ds = Ls + C::BM;
 
-    // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys.
-    f32x16 s = (f32x16){}, dp = (f32x16){};
+    // S = Q K^T and dP = dO V^T: QB blocks of 32 queries x this wave's 32 keys.
+    f32x16 s[QB], dp[QB];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)(Qs + lc * C::kRowPitch + 16 * ks + 8 * lg);
-      const bf16x8 ga = *(const bf16x8*)(Gs + lc * C::kRowPitch + 16 * ks + 8 * lg);
-      s = mfma32(qa, kb[ks], s);
-      dp = mfma32(ga, vb[ks], dp);
+    for (int b = 0; b < QB; ++b) {
+      s[b] = (f32x16){};
+      dp[b] = (f32x16){};
     }
-    // P = exp2(s * scale * log2 e - LSE * log2 e); dS = P (dP - D).  Each is
-    // kept as a bf16 pair (rounded value, rounded residual).
-    const bool diag = CAUSAL && (q0 < k0 + wave * 32 + 31);
-    uint32_t pw[8], pl[8], dsw[8], dsl[8];
+    const __bf16* qrow = Qs + row_lane_off;
+    const __bf16* grow = Gs + row_lane_off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 l4 = *(const f32x4*)(Ls + 8 * i + 4 * lg);
-      const f32x4 d4 = *(const f32x4*)(Ds + 8 * i + 4 * lg);
-      float p[4], ds[4];
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * i + j;
-        float pv = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[j]));
-        const int q = q0 + 8 * i + 4 * lg + j;
-        if ((diag && key > q) || key >= N) pv = 0.f;
-        p[j] = pv;
-        ds[j] = pv * (dp[r] - d4[j]);
+      for (int b = 0; b < QB; ++b) {
+        const int off = 32 * b * C::kRowPitch + 16 * ks;
+        const bf16x8 qa = *(const bf16x8*)(qrow + off);
+        const bf16x8 ga = *(const bf16x8*)(grow + off);
+        s[b] = mfma32(qa, kb[ks], s[b]);
+        dp[b] = mfma32(ga, vb[ks], dp[b]);
+      }
+
+    // Per 32-query block: P = exp2(s * scale * log2 e - LSE * log2 e) and
+    // dS = P (dP - D), each kept as a bf16 pair (rounded value, rounded
+    // residual); dS^T goes to LDS for dQ; then dV^T += dO^T P and
+    // dK^T += Q^T dS with the A operands read down the columns, in the key
+    // order P's accumulator layout leaves in each lane half.  Causal masking
+    // (key > query) and keys past N give P = 0.
+    const __bf16* gtr = Gs + tr_off_p;
+    const __bf16* qtr = Qs + tr_off_p;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int qb0 = q0 + 32 * b;
+      PdsOperands ops;
+      uint32_t pw[8], pl[8], dsw[8], dsl[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 l4 = *(const f32x4*)(Ls + 32 * b + 8 * i + 4 * lg);
+        const f32x4 d4 = *(const f32x4*)(Ds + 32 * b + 8 * i + 4 * lg);
+        float p[4], ds[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * i + j;
+          const float pe = fast_exp2(__builtin_fmaf(s[b][r], scale_log2, -l4[j]));
+          const int q = qb0 + 8 * i + 4 * lg + j;
+          const bool keep = key_ok & (!CAUSAL | (q >= key));
+          const float pv = keep ? pe : 0.f;
+          p[j] = pv;
+          ds[j] = pv * (dp[b][r] - d4[j]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t ph = pack_bf16x2(p[2 * hh], p[2 * hh + 1]);
+          const uint32_t dh = pack_bf16x2(ds[2 * hh], ds[2 * hh + 1]);
+          pw[2 * i + hh] = ph;
+          pl[2 * i + hh] = pack_bf16x2(p[2 * hh] - bf16_lo(ph), p[2 * hh + 1] - bf16_hi(ph));
+          dsw[2 * i + hh] = dh;
+          dsl[2 * i + hh] = pack_bf16x2(ds[2 * hh] - bf16_lo(dh), ds[2 * hh + 1] - bf16_hi(dh));
+        }
+        // dS^T[key][q .. q+3] (both terms) for the dQ product.
+        const int off = (wave * 32 + lc) * C::kDsPitch + 32 * b + 8 * i + 4 * lg;
+        *(u32x2*)(dSt + off) = (u32x2){dsw[2 * i], dsw[2 * i + 1]};
+        *(u32x2*)(dSt_lo + off) = (u32x2){dsl[2 * i], dsl[2 * i + 1]};
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t ph = pack_bf16x2(p[2 * h], p[2 * h + 1]);
-        const uint32_t dh = pack_bf16x2(ds[2 * h], ds[2 * h + 1]);
-        pw[2 * i + h] = ph;
-        pl[2 * i + h] = pack_bf16x2(p[2 * h] - bf16_lo(ph), p[2 * h + 1] - bf16_hi(ph));
-        dsw[2 * i + h] = dh;
-        dsl[2 * i + h] = pack_bf16x2(ds[2 * h] - bf16_lo(dh), ds[2 * h + 1] - bf16_hi(dh));
+      for (int c = 0; c < 2; ++c) {
+        ops.p[c] = __builtin_bit_cast(bf16x8, ((u32x4){pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]}));
+        ops.pl[c] = __builtin_bit_cast(bf16x8, ((u32x4){pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]}));
+        ops.ds[c] =
+            __builtin_bit_cast(bf16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
+        ops.dsl[c] =
+            __builtin_bit_cast(bf16x8, ((u32x4){dsl[4 * c], dsl[4 * c + 1], dsl[4 * c + 2], dsl[4 * c + 3]}));
       }
-      // dS^T[key][q .. q+3] (both terms) for the dQ product.
-      const int off = (wave * 32 + lc) * C::kDsPitch + 8 * i + 4 * lg;
-      *(u32x2*)(dSt + off) = (u32x2){dsw[2 * i], dsw[2 * i + 1]};
-      *(u32x2*)(dSt_lo + off) = (u32x2){dsl[2 * i], dsl[2 * i + 1]};
-    }
-    // B operands (k = query, in the accumulator's lane order).
-    bf16x8 pB[2], pBl[2], dsB[2], dsBl[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      pB[c] = __builtin_bit_cast(bf16x8, ((u32x4){pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]}));
-      pBl[c] = __builtin_bit_cast(bf16x8, ((u32x4){pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]}));
-      dsB[c] = __builtin_bit_cast(bf16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
-      dsBl[c] = __builtin_bit_cast(bf16x8, ((u32x4){dsl[4 * c], dsl[4 * c + 1], dsl[4 * c + 2], dsl[4 * c + 3]}));
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (A operands read down the columns).
+      for (int c = 0; c < 2; ++c) {
+        const int r0 = 32 * b + 16 * c;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int r_lo = 16 * c + 4 * lg, r_hi = 16 * c + 8 + 4 * lg;
-#pragma unroll
-      for (int dm = 0; dm < D / 32; ++dm) {
-        const bf16x8 ga = lds_read_down(Gs, C::kRowPitch, 32 * dm, r_lo, r_hi, lane);
-        const bf16x8 qa = lds_read_down(Qs, C::kRowPitch, 32 * dm, r_lo, r_hi, lane);
-        dv_acc[dm] = mfma32(ga, pB[c], dv_acc[dm]);
-        dv_acc[dm] = mfma32(ga, pBl[c], dv_acc[dm]);
-        dk_acc[dm] = mfma32(qa, dsB[c], dk_acc[dm]);
-        dk_acc[dm] = mfma32(qa, dsBl[c], dk_acc[dm]);
+        for (int dm = 0; dm < D / 32; ++dm) {
+          const int lo = r0 * C::kRowPitch + 32 * dm, hi = (r0 + 8) * C::kRowPitch + 32 * dm;
+          const bf16x8 ga = lds_tr_pair(gtr, lo, hi);
+          const bf16x8 qa = lds_tr_pair(qtr, lo, hi);
+          dv_acc[dm] = mfma32(ga, ops.p[c], dv_acc[dm]);
+          dk_acc[dm] = mfma32(qa, ops.ds[c], dk_acc[dm]);
+          dv_acc[dm] = mfma32(ga, ops.pl[c], dv_acc[dm]);
+          dk_acc[dm] = mfma32(qa, ops.dsl[c], dk_acc[dm]);
+        }
       }
     }
     if (qt + 1 < qt_end) bwd_store_stage<D>(st, stages + ((it + 1) & 1) * C::kStageBytes, tid);
     __syncthreads();   // dS^T complete
 
-    // dQ(32 x D) for this query tile from the workgroup's 128 keys.  D = 128:
-    // wave w forms feature block w over all keys; D = 64: feature block
-    // w % 2 over key half w / 2.
+    // dQ (BM x D) for this query tile from the workgroup's 128 keys: the
+    // (query block, feature block) pairs are dealt out to the waves, each
+    // summing over all keys; independent blocks of a wave interleave.
     {
-      constexpr int kBlocks = D / 32;
-      constexpr int kSplit = C::kWaves / kBlocks;           // key groups
-      constexpr int kSteps = C::BN / 16 / kSplit;
-      const int dm = wave % kBlocks;
-      const int kgrp = wave / kBlocks;
-      f32x16 acc = (f32x16){};
+      f32x16 acc[C::kDqPerWave];
+      int qbk[C::kDqPerWave], dmk[C::kDqPerWave];
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) {
-        const int kk = (kgrp * kSteps + j) * 16;
-        const bf16x8 a = lds_read_down(dSt, C::kDsPitch, 0, kk + 8 * lg, kk + 8 * lg + 4, lane);
-        const bf16x8 al = lds_read_down(dSt_lo, C::kDsPitch, 0, kk + 8 * lg, kk + 8 * lg + 4, lane);
-        const bf16x8 b = *(const bf16x8*)(Kt + (32 * dm + lc) * C::kKtPitch + kk + 8 * lg);
-        acc = mfma32(a, b, acc);
-        acc = mfma32(al, b, acc);
+      for (int j = 0; j < C::kDqPerWave; ++j) {
+        const int blk = wave * C::kDqPerWave + j;
+        qbk[j] = blk / (D / 32);
+        dmk[j] = blk % (D / 32);
+        acc[j] = (f32x16){};
+      }
+      const __bf16* dsp = dSt + tr_off_n;
+      const __bf16* dslp = dSt_lo + tr_off_n;
+      const __bf16* ktp = Kt + kt_lane_off;
+#pragma unroll
+      for (int ks = 0; ks < C::BN / 16; ++ks) {
+        const int kk = 16 * ks;
+#pragma unroll
+        for (int j = 0; j < C::kDqPerWave; ++j) {
+          const int lo = kk * C::kDsPitch + 32 * qbk[j], hi = (kk + 4) * C::kDsPitch + 32 * qbk[j];
+          const bf16x8 a = lds_tr_pair(dsp, lo, hi);
+          const bf16x8 al = lds_tr_pair(dslp, lo, hi);
+          const bf16x8 b = *(const bf16x8*)(ktp + 32 * dmk[j] * C::kKtPitch + kk);
+          acc[j] = mfma32(a, b, acc[j]);
+          acc[j] = mfma32(al, b, acc[j]);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + 32 * dm + lc, acc[r]);
-      }
+      for (int j = 0; j < C::kDqPerWave; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + 32 * qbk[j] + 8 * (r >> 2) + 4 * lg + (r & 3);
+          batomic_add(h.dq, (uint32_t)(q * D + 32 * dmk[j] + lc) * 4u, acc[j][r]);
+        }
     }
   }
 
