@@ -13,12 +13,13 @@
 //     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so the
 //     32x32 accumulator puts one query per lane column: the row max and row
 //     sum are in-lane reductions plus one permlane32 swap.
-//   * K and V tiles of BN keys are staged in LDS and shared by the 8 waves.
-//     K runs one tile ahead of V: while a wave turns tile t's scores into
-//     probabilities (VALU, exp2) it already issues the MFMAs of tile t+1's
-//     scores, so the matrix cores and the vector ALU overlap inside a wave
-//     as well as across the two waves sharing a SIMD.  Double buffers for K
-//     and for V with one barrier per tile.
+//   * K and V tiles of BN keys are staged in LDS (double buffered) and
+//     shared by the 8 waves.  Each key-tile step has two barrier-separated
+//     phases: a matrix phase (O += P(t) V(t) and S(t+1) = K(t+1) Q^T) and a
+//     vector phase (the online softmax of S(t+1)).  Waves 4-7 run one phase
+//     behind waves 0-3, so the two waves sharing a SIMD alternate between the
+//     matrix cores and the vector ALU.  Waves 0-3 stage the K tiles and waves
+//     4-7 the V tiles, each in its own vector phase.
 //   * K and V are stored row-major with padding.  The A operand of
 //     O^T += V^T P^T (V transposed) is read with ds_read_b64_tr_b16, which
 //     hands each lane four consecutive keys of one feature column; the two
@@ -61,35 +62,36 @@ struct FwdCfg {
   static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
 };
 
-template <int D, int BN>
+template <int D, int BN, int THREADS>
 struct TileStage {
-  u32x4 c[FwdCfg<D, BN>::kPerThread];
+  static constexpr int kChunks = BN * D / 8;              // 16-byte chunks per tile
+  static constexpr int kPer = (kChunks + THREADS - 1) / THREADS;
+  u32x4 c[kPer];
 };
 
 // Global -> registers: this thread's 16-byte chunks of a BN x D tile (rows
 // past the head's end read as zero through the buffer descriptor).
-template <int D, int BN>
-__device__ __forceinline__ void load_tile(TileStage<D, BN>& st, __amdgpu_buffer_rsrc_t r, int j0, int tid) {
-  using C = FwdCfg<D, BN>;
+template <int D, int BN, int THREADS>
+__device__ __forceinline__ void load_tile(TileStage<D, BN, THREADS>& st, __amdgpu_buffer_rsrc_t r, int j0, int tid) {
+  using S = TileStage<D, BN, THREADS>;
 #pragma unroll
-  for (int i = 0; i < C::kPerThread; ++i) {
-    const int c = tid + i * C::kThreads;
+  for (int i = 0; i < S::kPer; ++i) {
+    const int c = tid + i * THREADS;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    if (C::kChunks % C::kThreads == 0 || c < C::kChunks)
-      st.c[i] = bload128(r, (uint32_t)((j0 + row) * D + col) * 2u);
+    if (S::kChunks % THREADS == 0 || c < S::kChunks) st.c[i] = bload128(r, (uint32_t)((j0 + row) * D + col) * 2u);
   }
 }
 
 // Registers -> LDS, row-major with `pitch` elements per row.
-template <int D, int BN, int PITCH>
-__device__ __forceinline__ void store_tile(const TileStage<D, BN>& st, __bf16* S, int tid) {
-  using C = FwdCfg<D, BN>;
+template <int D, int BN, int THREADS>
+__device__ __forceinline__ void store_tile(const TileStage<D, BN, THREADS>& st, __bf16* S, int pitch, int tid) {
+  using T = TileStage<D, BN, THREADS>;
 #pragma unroll
-  for (int i = 0; i < C::kPerThread; ++i) {
-    const int c = tid + i * C::kThreads;
-    if (C::kChunks % C::kThreads == 0 || c < C::kChunks) {
+  for (int i = 0; i < T::kPer; ++i) {
+    const int c = tid + i * THREADS;
+    if (T::kChunks % THREADS == 0 || c < T::kChunks) {
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)(S + row * PITCH + col) = st.c[i];
+      *(u32x4*)(S + row * pitch + col) = st.c[i];
     }
   }
 }
@@ -189,54 +191,6 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const bf16x8 (&p
 }
 
 template <int D, int BN, bool CAUSAL>
-struct FwdState {
-  const __bf16* Kbuf[2];
-  __bf16* Kw[2];
-  const __bf16* Vbuf[2];
-  __bf16* Vw[2];
-  __amdgpu_buffer_rsrc_t rk, rv;
-  int N, num_kt, q_wave0, q_idx, tid, v_lane_off, lc, lg;
-  float scale_log2;
-};
-
-// One key tile: prefetch K(t+2) and V(t+1) into registers, turn S(t) into
-// P while issuing S(t+1) = K(t+1) Q^T, accumulate P V(t), then publish the
-// prefetched tiles to LDS and synchronise.
-template <int D, int BN, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile_step(const FwdState<D, BN, CAUSAL>& g, int t, f32x16 (&sc)[BN / 32],
-                                              f32x16 (&sn)[BN / 32], const bf16x8 (&qb)[D / 16],
-                                              f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
-                                              TileStage<D, BN>& stk, TileStage<D, BN>& stv) {
-  using C = FwdCfg<D, BN>;
-  const int j0 = t * BN;
-  const bool has_next = t + 1 < g.num_kt;
-  const bool has_next2 = t + 2 < g.num_kt;
-  if (has_next2) load_tile<D, BN>(stk, g.rk, j0 + 2 * BN, g.tid);
-  if (has_next) load_tile<D, BN>(stv, g.rv, j0 + BN, g.tid);
-  const bool live = !CAUSAL || j0 <= g.q_wave0 + 31;
-  if (live) {
-    const bool need_mask = (j0 + BN > g.N) || (CAUSAL && j0 + BN - 1 > g.q_wave0);
-    if (need_mask) mask_tile<BN>(sc, j0, CAUSAL ? min(g.q_idx, g.N - 1) : g.N - 1, g.lg);
-    softmax_max<D, BN>(sc, m_run, l_run, oacc, g.scale_log2);
-    // One straight-line block: the next tile's score MFMAs, this tile's
-    // exponentials, and this tile's P V MFMAs, for the scheduler to
-    // interleave.  S(t+1) is formed even when no live tile t+1 follows (the
-    // last tile, or the last live tile of a wave on the causal diagonal):
-    // one wasted tile of MFMAs per wave buys a branch-free block; the stale
-    // result is never read.
-    bf16x8 pb[BN / 16];
-    score_tile<D, BN>(sn, g.Kbuf[(t + 1) & 1], qb, g.lc, g.lg);
-    softmax_exp<BN>(sc, pb, m_run, l_run, g.scale_log2);
-    pv_tile<D, BN>(oacc, pb, g.Vbuf[t & 1], g.v_lane_off);
-  }
-  // (A wave that is not live for tile t is not live for t+1 either: keys
-  // only grow, so S(t+1) is never needed when tile t is skipped.)
-  if (has_next2) store_tile<D, BN, C::kKPitch>(stk, g.Kw[t & 1], g.tid);
-  if (has_next) store_tile<D, BN, C::kVPitch>(stv, g.Vw[(t + 1) & 1], g.tid);
-  __syncthreads();
-}
-
-template <int D, int BN, bool CAUSAL>
 __global__ void __launch_bounds__(512)
 fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
@@ -244,13 +198,13 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using C = FwdCfg<D, BN>;
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
-  FwdState<D, BN, CAUSAL> g;
-  g.tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // uniform per wave
-  const int lane = g.tid & 63;
-  g.v_lane_off = tr_lane_off(lane, C::kVPitch, 4);
-  g.lc = lane & 31;     // lane column: query within the wave
-  g.lg = lane >> 5;     // lane half
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int group = wave >> 2;   // 0: waves 0-3 (one per SIMD), 1: waves 4-7
+  const int lane = tid & 63;
+  const int lc = lane & 31;      // lane column: query within the wave
+  const int lg = lane >> 5;      // lane half
+  const int gtid = tid & 255;    // thread index within the group
 
   const int bid = blockIdx.x;
   const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
@@ -258,26 +212,24 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
-  g.rk = make_rsrc(K + head_off, head_bytes);
-  g.rv = make_rsrc(V + head_off, head_bytes);
-  g.N = N;
-  g.scale_log2 = scale_log2;
-  g.q_wave0 = qt * C::BM + wave * 32;
-  g.q_idx = g.q_wave0 + g.lc;
-  g.Kw[0] = smem;
-  g.Kw[1] = smem + C::kKTile;
-  g.Vw[0] = smem + 2 * C::kKTile;
-  g.Vw[1] = smem + 2 * C::kKTile + C::kVTile;
-  for (int i = 0; i < 2; ++i) {
-    g.Kbuf[i] = g.Kw[i];
-    g.Vbuf[i] = g.Vw[i];
-  }
+  // Group 0 stages the K tiles, group 1 the V tiles.
+  const __amdgpu_buffer_rsrc_t rmine = make_rsrc((group == 0 ? K : V) + head_off, head_bytes);
+  __bf16* Kbuf0 = smem;
+  __bf16* Kbuf1 = smem + C::kKTile;
+  __bf16* Vbuf0 = smem + 2 * C::kKTile;
+  __bf16* Vbuf1 = smem + 2 * C::kKTile + C::kVTile;
+  __bf16* mybuf0 = group == 0 ? Kbuf0 : Vbuf0;
+  __bf16* mybuf1 = group == 0 ? Kbuf1 : Vbuf1;
+  const int v_lane_off = tr_lane_off(lane, C::kVPitch, 4);
+
+  const int q_wave0 = qt * C::BM + wave * 32;
+  const int q_idx = q_wave0 + lc;
 
   // Q^T as MFMA B operand: lane holds Q[q][16 ks + 8 lg .. +7] (zeros past N).
   bf16x8 qb[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
-    qb[ks] = __builtin_bit_cast(bf16x8, bload128(rq, (uint32_t)(g.q_idx * D + 16 * ks + 8 * g.lg) * 2u));
+    qb[ks] = __builtin_bit_cast(bf16x8, bload128(rq, (uint32_t)(q_idx * D + 16 * ks + 8 * lg) * 2u));
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -287,48 +239,77 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   const int q_tile_end = min(N, (qt + 1) * C::BM);
   const int key_end = CAUSAL ? q_tile_end : N;
-  g.num_kt = (key_end + BN - 1) / BN;
+  const int num_kt = (key_end + BN - 1) / BN;
+  const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
+  auto live = [&](int t) { return !CAUSAL || t * BN <= q_wave0 + 31; };
+  auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
-  // Prologue: K(0), V(0), K(1) into LDS; S(0).
-  {
-    TileStage<D, BN> k0, v0;
-    load_tile<D, BN>(k0, g.rk, 0, g.tid);
-    load_tile<D, BN>(v0, g.rv, 0, g.tid);
-    store_tile<D, BN, C::kKPitch>(k0, g.Kw[0], g.tid);
-    store_tile<D, BN, C::kVPitch>(v0, g.Vw[0], g.tid);
-    if (g.num_kt > 1) {
-      load_tile<D, BN>(k0, g.rk, BN, g.tid);
-      store_tile<D, BN, C::kKPitch>(k0, g.Kw[1], g.tid);
-    }
+  // Each group stages tiles 0 and 1 of its tensor, and holds tile 2 in
+  // registers until its first write slot.
+  TileStage<D, BN, 256> stage;
+  load_tile<D, BN, 256>(stage, rmine, 0, gtid);
+  store_tile<D, BN, 256>(stage, mybuf0, group == 0 ? C::kKPitch : C::kVPitch, gtid);
+  if (num_kt > 1) {
+    load_tile<D, BN, 256>(stage, rmine, BN, gtid);
+    store_tile<D, BN, 256>(stage, mybuf1, group == 0 ? C::kKPitch : C::kVPitch, gtid);
   }
+  if (num_kt > 2) load_tile<D, BN, 256>(stage, rmine, 2 * BN, gtid);
   __syncthreads();
-  f32x16 sa[BN / 32], sb[BN / 32];
-  score_tile<D, BN>(sa, g.Kbuf[0], qb, g.lc, g.lg);
 
-  TileStage<D, BN> stk, stv;
-  for (int t = 0; t < g.num_kt; t += 2) {
-    fwd_tile_step<D, BN, CAUSAL>(g, t, sa, sb, qb, oacc, m_run, l_run, stk, stv);
-    if (t + 1 < g.num_kt) fwd_tile_step<D, BN, CAUSAL>(g, t + 1, sb, sa, qb, oacc, m_run, l_run, stk, stv);
+  // S(0) and P(0).
+  f32x16 s[BN / 32];
+  bf16x8 pb[BN / 16];
+  score_tile<D, BN>(s, Kbuf0, qb, lc, lg);
+  if (masked(0)) mask_tile<BN>(s, 0, qlim, lg);
+  softmax_max<D, BN>(s, m_run, l_run, oacc, scale_log2);
+  softmax_exp<BN>(s, pb, m_run, l_run, scale_log2);
+
+  // The two waves on each SIMD (waves w and w + 4) alternate: group 1 runs
+  // one barrier interval behind group 0, so while one issues the step's
+  // MFMAs the other is in its exponentials.  Every wave passes the same
+  // number of barriers (group 1 one extra here, group 0 one extra at the
+  // end).  Buffer t % 2 holds tile t; a tile's buffer is rewritten only in
+  // the interval after both groups' last read of the tile it held.
+  if (group == 1) __syncthreads();
+
+  for (int t = 0; t < num_kt; ++t) {
+    // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.
+    const bool next = t + 1 < num_kt && live(t + 1);
+    if (live(t)) pv_tile<D, BN>(oacc, pb, (t & 1) ? Vbuf1 : Vbuf0, v_lane_off);
+    if (next) score_tile<D, BN>(s, ((t + 1) & 1) ? Kbuf1 : Kbuf0, qb, lc, lg);
+    __syncthreads();
+    // Phase 2 (vector ALU): P(t+1); publish tile t+2 of this group's
+    // tensor and fetch tile t+3.
+    if (next) {
+      if (masked(t + 1)) mask_tile<BN>(s, (t + 1) * BN, qlim, lg);
+      softmax_max<D, BN>(s, m_run, l_run, oacc, scale_log2);
+      softmax_exp<BN>(s, pb, m_run, l_run, scale_log2);
+    }
+    if (t + 2 < num_kt) {
+      store_tile<D, BN, 256>(stage, (t & 1) ? mybuf1 : mybuf0, group == 0 ? C::kKPitch : C::kVPitch, gtid);
+      if (t + 3 < num_kt) load_tile<D, BN, 256>(stage, rmine, (t + 3) * BN, gtid);
+    }
+    __syncthreads();
   }
+  if (group == 0) __syncthreads();
 
   // Epilogue: O / l rounded to bf16, and LSE = m + ln l (natural log).
   const float l_tot = sum_with_lane_xor32(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (g.q_idx < N) {
-    __bf16* orow = O + head_off + (size_t)g.q_idx * D;
+  if (q_idx < N) {
+    __bf16* orow = O + head_off + (size_t)q_idx * D;
 #pragma unroll
     for (int dm = 0; dm < D / 32; ++dm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * inv_l, oacc[dm][4 * i + 1] * inv_l),
                    pack_bf16x2(oacc[dm][4 * i + 2] * inv_l, oacc[dm][4 * i + 3] * inv_l)};
-        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * g.lg) = w;
+        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * lg) = w;
       }
-    if (LSE != nullptr && g.lg == 0)
-      LSE[(size_t)bh * N + g.q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+    if (LSE != nullptr && lg == 0)
+      LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // fp32 forward: float32 storage and arithmetic throughout (no bf16 rounding
