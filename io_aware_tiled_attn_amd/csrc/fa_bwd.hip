@@ -140,12 +140,6 @@ __device__ __forceinline__ void bwd_store_stage(const BwdStage<D>& st, char* sta
   else if (tid < 2 * C::BM) Ds[tid - C::BM] = st.dlt;
 }
 
-// B operands (k = query, in the accumulator's lane order) for the P and dS
-// terms of one 32-query block: rounded value and rounded residual.
-struct PdsOperands {
-  bf16x8 p[2], pl[2], ds[2], dsl[2];
-};
-
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -232,92 +226,107 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     const float* Ls = (const float*)(Gs + C::kTile);
     const float* Ds = Ls + C::BM;
 
-    // S = Q K^T and dP = dO V^T: QB blocks of 32 queries x this wave's 32 keys.
-    f32x16 s[QB], dp[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      s[b] = (f32x16){};
-      dp[b] = (f32x16){};
-    }
+    // Two 32-query blocks per step.  For block b:
+    //   S = Q K^T and dP = dO V^T (32 queries x this wave's 32 keys);
+    //   P = exp2(s * scale * log2 e - LSE * log2 e), dS = P (dP - D), each
+    //   kept as a bf16 pair (rounded value, rounded residual), with causal
+    //   masking (key > query) and keys past N giving P = 0; dS^T to LDS;
+    //   dV^T += dO^T P and dK^T += Q^T dS, the A operands read down the
+    //   columns in the key order P's accumulator layout leaves in each lane.
+    // With one wave per SIMD, the matrix and vector work of the two blocks
+    // are interleaved by hand: block 1's score MFMAs run in four chunks,
+    // each beside a quarter of block 0's vector work, and block 0's dV/dK
+    // MFMAs beside block 1's vector work; scheduling barriers keep the
+    // chunks in order.
+    static_assert(QB == 2, "the step interleaves exactly two query blocks");
     const __bf16* qrow = Qs + row_lane_off;
     const __bf16* grow = Gs + row_lane_off;
+    const __bf16* gtr = Gs + tr_off_p;
+    const __bf16* qtr = Qs + tr_off_p;
+    constexpr int KS = D / 16;                 // k-steps of the score products
+    constexpr int KSC = (KS + 3) / 4;          // k-steps per chunk
+    constexpr int DM = D / 32;
+    constexpr int UPC = (2 * DM + 3) / 4;      // (c, dm) dV/dK pairs per chunk
+
+    f32x16 sc[QB], dpc[QB];
+    auto score_steps = [&](int b, int ks0, int ks1) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
+      for (int ks = ks0; ks < ks1; ++ks) {
         const int off = 32 * b * C::kRowPitch + 16 * ks;
         const bf16x8 qa = *(const bf16x8*)(qrow + off);
         const bf16x8 ga = *(const bf16x8*)(grow + off);
-        s[b] = mfma32(qa, kb[ks], s[b]);
-        dp[b] = mfma32(ga, vb[ks], dp[b]);
+        sc[b] = mfma32(qa, kb[ks], sc[b]);
+        dpc[b] = mfma32(ga, vb[ks], dpc[b]);
       }
+    };
+    uint32_t pw[QB][8], pl[QB][8], dsw[QB][8], dsl[QB][8];
+    auto vector_group = [&](int b, int i) {
+      const int qb0 = q0 + 32 * b;
+      const f32x4 l4 = *(const f32x4*)(Ls + 32 * b + 8 * i + 4 * lg);
+      const f32x4 d4 = *(const f32x4*)(Ds + 32 * b + 8 * i + 4 * lg);
+      float p[4], ds[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * i + j;
+        const float pe = fast_exp2(__builtin_fmaf(sc[b][r], scale_log2, -l4[j]));
+        const int q = qb0 + 8 * i + 4 * lg + j;
+        const bool keep = key_ok & (!CAUSAL | (q >= key));
+        const float pv = keep ? pe : 0.f;
+        p[j] = pv;
+        ds[j] = pv * (dpc[b][r] - d4[j]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t ph = pack_bf16x2(p[2 * hh], p[2 * hh + 1]);
+        const uint32_t dh = pack_bf16x2(ds[2 * hh], ds[2 * hh + 1]);
+        pw[b][2 * i + hh] = ph;
+        pl[b][2 * i + hh] = pack_bf16x2(p[2 * hh] - bf16_lo(ph), p[2 * hh + 1] - bf16_hi(ph));
+        dsw[b][2 * i + hh] = dh;
+        dsl[b][2 * i + hh] = pack_bf16x2(ds[2 * hh] - bf16_lo(dh), ds[2 * hh + 1] - bf16_hi(dh));
+      }
+      // dS^T[key][q .. q+3] (both terms) for the dQ product.
+      const int off = (wave * 32 + lc) * C::kDsPitch + 32 * b + 8 * i + 4 * lg;
+      *(u32x2*)(dSt + off) = (u32x2){dsw[b][2 * i], dsw[b][2 * i + 1]};
+      *(u32x2*)(dSt_lo + off) = (u32x2){dsl[b][2 * i], dsl[b][2 * i + 1]};
+    };
+    auto operand = [&](const uint32_t (&w)[8], int c) {
+      return __builtin_bit_cast(bf16x8, ((u32x4){w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]}));
+    };
+    auto update_pairs = [&](int b, int u0, int u1) {
+#pragma unroll
+      for (int u = u0; u < u1; ++u) {
+        const int c = u / DM, dm = u % DM;
+        const int r0 = 32 * b + 16 * c;
+        const int lo = r0 * C::kRowPitch + 32 * dm, hi = (r0 + 8) * C::kRowPitch + 32 * dm;
+        const bf16x8 ga = lds_tr_pair(gtr, lo, hi);
+        const bf16x8 qa = lds_tr_pair(qtr, lo, hi);
+        dv_acc[dm] = mfma32(ga, operand(pw[b], c), dv_acc[dm]);
+        dk_acc[dm] = mfma32(qa, operand(dsw[b], c), dk_acc[dm]);
+        dv_acc[dm] = mfma32(ga, operand(pl[b], c), dv_acc[dm]);
+        dk_acc[dm] = mfma32(qa, operand(dsl[b], c), dk_acc[dm]);
+      }
+    };
 
-    // Per 32-query block: P = exp2(s * scale * log2 e - LSE * log2 e) and
-    // dS = P (dP - D), each kept as a bf16 pair (rounded value, rounded
-    // residual); dS^T goes to LDS for dQ; then dV^T += dO^T P and
-    // dK^T += Q^T dS with the A operands read down the columns, in the key
-    // order P's accumulator layout leaves in each lane half.  Causal masking
-    // (key > query) and keys past N give P = 0.
-    const __bf16* gtr = Gs + tr_off_p;
-    const __bf16* qtr = Qs + tr_off_p;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      const int qb0 = q0 + 32 * b;
-      PdsOperands ops;
-      uint32_t pw[8], pl[8], dsw[8], dsl[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 l4 = *(const f32x4*)(Ls + 32 * b + 8 * i + 4 * lg);
-        const f32x4 d4 = *(const f32x4*)(Ds + 32 * b + 8 * i + 4 * lg);
-        float p[4], ds[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * i + j;
-          const float pe = fast_exp2(__builtin_fmaf(s[b][r], scale_log2, -l4[j]));
-          const int q = qb0 + 8 * i + 4 * lg + j;
-          const bool keep = key_ok & (!CAUSAL | (q >= key));
-          const float pv = keep ? pe : 0.f;
-          p[j] = pv;
-          ds[j] = pv * (dp[b][r] - d4[j]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint32_t ph = pack_bf16x2(p[2 * hh], p[2 * hh + 1]);
-          const uint32_t dh = pack_bf16x2(ds[2 * hh], ds[2 * hh + 1]);
-          pw[2 * i + hh] = ph;
-          pl[2 * i + hh] = pack_bf16x2(p[2 * hh] - bf16_lo(ph), p[2 * hh + 1] - bf16_hi(ph));
-          dsw[2 * i + hh] = dh;
-          dsl[2 * i + hh] = pack_bf16x2(ds[2 * hh] - bf16_lo(dh), ds[2 * hh + 1] - bf16_hi(dh));
-        }
-        // dS^T[key][q .. q+3] (both terms) for the dQ product.
-        const int off = (wave * 32 + lc) * C::kDsPitch + 32 * b + 8 * i + 4 * lg;
-        *(u32x2*)(dSt + off) = (u32x2){dsw[2 * i], dsw[2 * i + 1]};
-        *(u32x2*)(dSt_lo + off) = (u32x2){dsl[2 * i], dsl[2 * i + 1]};
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        ops.p[c] = __builtin_bit_cast(bf16x8, ((u32x4){pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]}));
-        ops.pl[c] = __builtin_bit_cast(bf16x8, ((u32x4){pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]}));
-        ops.ds[c] =
-            __builtin_bit_cast(bf16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
-        ops.dsl[c] =
-            __builtin_bit_cast(bf16x8, ((u32x4){dsl[4 * c], dsl[4 * c + 1], dsl[4 * c + 2], dsl[4 * c + 3]}));
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r0 = 32 * b + 16 * c;
-#pragma unroll
-        for (int dm = 0; dm < D / 32; ++dm) {
-          const int lo = r0 * C::kRowPitch + 32 * dm, hi = (r0 + 8) * C::kRowPitch + 32 * dm;
-          const bf16x8 ga = lds_tr_pair(gtr, lo, hi);
-          const bf16x8 qa = lds_tr_pair(qtr, lo, hi);
-          dv_acc[dm] = mfma32(ga, ops.p[c], dv_acc[dm]);
-          dk_acc[dm] = mfma32(qa, ops.ds[c], dk_acc[dm]);
-          dv_acc[dm] = mfma32(ga, ops.pl[c], dv_acc[dm]);
-          dk_acc[dm] = mfma32(qa, ops.dsl[c], dk_acc[dm]);
-        }
-      }
+      sc[b] = (f32x16){};
+      dpc[b] = (f32x16){};
     }
+    score_steps(0, 0, KS);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      score_steps(1, min(KS, j * KSC), min(KS, (j + 1) * KSC));
+      vector_group(0, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      update_pairs(0, min(2 * DM, j * UPC), min(2 * DM, (j + 1) * UPC));
+      vector_group(1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    update_pairs(1, 0, 2 * DM);
     if (qt + 1 < qt_end) bwd_store_stage<D>(st, stages + ((it + 1) & 1) * C::kStageBytes, tid);
     __syncthreads();   // dS^T complete
 
