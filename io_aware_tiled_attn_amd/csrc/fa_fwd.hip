@@ -44,6 +44,9 @@
 namespace fa {
 
 constexpr float kMaxSlack = 8.0f;
+#ifndef FWD_LOOKAHEAD
+#define FWD_LOOKAHEAD 8
+#endif
 
 template <int D, int BN>
 struct FwdCfg {
@@ -173,21 +176,47 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[BN / 32], bf16x8 (
   l_run += rowsum;
 }
 
-// O^T += V^T P^T for one tile.  V^T's operand for k-step c holds, in lane
-// half g, keys 16c + 4g + 0..3 and 16c + 8 + 4g + 0..3: the keys P's
-// accumulator layout leaves in that lane half.
-template <int D, int BN>
-__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vs,
-                                        int v_lane_off) {
+// Both products of a matrix phase, O += P(t) V(t) then S(t+1) = K(t+1) Q^T,
+// as one stream of MFMAs whose LDS operands are read kLookahead products
+// ahead, so the read latency hides behind the preceding MFMAs instead of
+// stalling each one.  Scheduling barriers keep the stream in this order.
+template <int D, int BN, int L>
+__device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vs,
+                                             int v_lane_off, f32x16 (&s)[BN / 32], const __bf16* Ks,
+                                             const bf16x8 (&qb)[D / 16], int lc, int lg) {
   using C = FwdCfg<D, BN>;
+  constexpr int kPv = BN / 16 * (D / 32);   // O += P V products
+  constexpr int kS = D / 16 * (BN / 32);    // S = K Q^T products
+  constexpr int kAll = kPv + kS;
   const __bf16* vp = Vs + v_lane_off;
-#pragma unroll
-  for (int c = 0; c < BN / 16; ++c)
-#pragma unroll
-    for (int dm = 0; dm < D / 32; ++dm) {
-      const bf16x8 a = lds_tr_pair(vp, (16 * c) * C::kVPitch + 32 * dm, (16 * c + 8) * C::kVPitch + 32 * dm);
-      oacc[dm] = mfma32(a, pb[c], oacc[dm]);
+  const __bf16* krow = Ks + lc * C::kKPitch + 8 * lg;
+  auto load = [&](int i) -> bf16x8 {
+    if (i < kPv) {
+      const int c = i / (D / 32), dm = i % (D / 32);
+      return lds_tr_pair(vp, (16 * c) * C::kVPitch + 32 * dm, (16 * c + 8) * C::kVPitch + 32 * dm);
     }
+    const int j = i - kPv, ks = j / (BN / 32), mb = j % (BN / 32);
+    return *(const bf16x8*)(krow + 32 * mb * C::kKPitch + 16 * ks);
+  };
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
+  bf16x8 ring[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) ring[i] = load(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kAll; ++i) {
+    const bf16x8 a = ring[i % L];
+    if (i < kPv) {
+      const int c = i / (D / 32), dm = i % (D / 32);
+      oacc[dm] = mfma32(a, pb[c], oacc[dm]);
+    } else {
+      const int j = i - kPv, ks = j / (BN / 32), mb = j % (BN / 32);
+      s[mb] = mfma32(a, qb[ks], s[mb]);
+    }
+    if (i + L < kAll) ring[i % L] = load(i + L);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <int D, int BN, bool CAUSAL>
@@ -241,7 +270,6 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int key_end = CAUSAL ? q_tile_end : N;
   const int num_kt = (key_end + BN - 1) / BN;
   const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
-  auto live = [&](int t) { return !CAUSAL || t * BN <= q_wave0 + 31; };
   auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
   // Each group stages tiles 0 and 1 of its tensor, and holds tile 2 in
@@ -273,14 +301,17 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (group == 1) __syncthreads();
 
   for (int t = 0; t < num_kt; ++t) {
-    // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.
-    const bool next = t + 1 < num_kt && live(t + 1);
-    if (live(t)) pv_tile<D, BN>(oacc, pb, (t & 1) ? Vbuf1 : Vbuf0, v_lane_off);
-    if (next) score_tile<D, BN>(s, ((t + 1) & 1) ? Kbuf1 : Kbuf0, qb, lc, lg);
+    // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
+    // wave runs the same instruction stream on every step: on causal tiles
+    // wholly above a wave's queries its P is all zero (the tile is masked
+    // like any other), and on the last step the score product reads a stale
+    // buffer and its result is not used.
+    matrix_phase<D, BN, FWD_LOOKAHEAD>(oacc, pb, (t & 1) ? Vbuf1 : Vbuf0, v_lane_off, s,
+                                       ((t + 1) & 1) ? Kbuf1 : Kbuf0, qb, lc, lg);
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1); publish tile t+2 of this group's
     // tensor and fetch tile t+3.
-    if (next) {
+    if (t + 1 < num_kt) {
       if (masked(t + 1)) mask_tile<BN>(s, (t + 1) * BN, qlim, lg);
       softmax_max<D, BN>(s, m_run, l_run, oacc, scale_log2);
       softmax_exp<BN>(s, pb, m_run, l_run, scale_log2);
