@@ -28,11 +28,11 @@
 //     16-lane group, and the two groups of a half-wave, on disjoint banks.
 //   * P is rounded to bf16 (RNE) and fed back as the B operand directly from
 //     the accumulator registers; O^T accumulates in fp32.
-//   * The running max is raised only when a tile's max exceeds it by more
-//     than kMaxSlack (log2 units).  Any reference value works in exact
-//     arithmetic (it cancels in O / l); keeping it within 2^kMaxSlack of the
-//     true max keeps every P <= 2^kMaxSlack, and the output rescale becomes
-//     rare instead of happening on almost every tile.
+//   * The running reference m is the first tile's max and is raised only
+//     when a tile's exponentials against it would sum past kPSumLimit in some
+//     lane (so every P stays <= kPSumLimit).  Any reference works in exact
+//     arithmetic (it cancels in O / l); a lazy one removes the per-tile max
+//     reduction and makes the output rescale rare.
 //   * Global reads use buffer descriptors sized to the head: reads past the
 //     last row return zeros, so ragged tails need no branches.
 //   * Workgroups are issued heaviest first (causal), with all query tiles of
@@ -43,7 +43,7 @@
 
 namespace fa {
 
-constexpr float kMaxSlack = 8.0f;
+constexpr float kPSumLimit = 256.0f;
 #ifndef FWD_LOOKAHEAD
 #define FWD_LOOKAHEAD 8
 #endif
@@ -129,35 +129,13 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[BN / 32], int j0, int qlim
     }
 }
 
-// Online-softmax step for one tile of scores (this lane's query column),
-// first half: raise the running max when the tile exceeds it by more than
-// kMaxSlack, rescaling O and l (rare after the first tile).
-template <int D, int BN>
-__device__ __forceinline__ void softmax_max(const f32x16 (&s)[BN / 32], float& m_run, float& l_run,
-                                            f32x16 (&oacc)[D / 32], float scale_log2) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < BN / 32; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-  mx = max_with_lane_xor32(mx) * scale_log2;
-  if (__ballot(mx > m_run + kMaxSlack)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-  }
-}
-
-// Second half: P = exp2(s * scale * log2 e - m) packed to bf16 B operands,
-// l += sum P.  Rows whose keys are all masked so far keep m = -inf; 0 is
-// used instead so exp2 gives 0 rather than NaN.
+// P = exp2(s * scale * log2 e - m) for one tile, rounded to bf16 and packed
+// as the B operands of the P V product.  Returns this lane's sum of P,
+// taken in fp32 before rounding so that l, and with it the saved
+// logsumexp, is not perturbed by the bf16 rounding of P.
 template <int BN>
-__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[BN / 32], bf16x8 (&pb)[BN / 16], float m_run,
-                                            float& l_run, float scale_log2) {
-  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+__device__ __forceinline__ float tile_exp(const f32x16 (&s)[BN / 32], bf16x8 (&pb)[BN / 16], float m,
+                                          float scale_log2) {
   float rowsum = 0.f;
 #pragma unroll
   for (int mb = 0; mb < BN / 32; ++mb)
@@ -166,14 +144,45 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[BN / 32], bf16x8 (
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e], scale_log2, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e + 1], scale_log2, -m_use));
+        const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e], scale_log2, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e + 1], scale_log2, -m));
         rowsum += p0 + p1;
         w[e] = pack_bf16x2(p0, p1);
       }
       pb[2 * mb + h] = __builtin_bit_cast(bf16x8, ((u32x4){w[0], w[1], w[2], w[3]}));
     }
-  l_run += rowsum;
+  return rowsum;
+}
+
+// Online-softmax step for one tile of scores (this lane's query column).
+// The exponentials are taken against the running reference m first.  If
+// every lane's sum of this tile's P stays within kPSumLimit, every P does
+// too and the tile is done: m, O and l are unchanged.  Otherwise (the first
+// tile, where m = -inf, or a tile whose scores climb well above m) m is
+// raised to the tile's max, O and l are rescaled by 2^(m_old - m_new), and
+// the exponentials are taken again.
+template <int D, int BN>
+__device__ __forceinline__ void softmax_step(const f32x16 (&s)[BN / 32], bf16x8 (&pb)[BN / 16], float& m_run,
+                                             float& l_run, f32x16 (&oacc)[D / 32], float scale_log2) {
+  float rs = tile_exp<BN>(s, pb, m_run, scale_log2);
+  if (__ballot(!(rs <= kPSumLimit))) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = max_with_lane_xor32(mx) * scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    // A query whose keys are all masked so far keeps m = -inf; 0 is used
+    // instead so exp2 gives 0 rather than NaN.
+    rs = tile_exp<BN>(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
+  }
+  l_run += rs;
 }
 
 // Both products of a matrix phase, O += P(t) V(t) then S(t+1) = K(t+1) Q^T,
@@ -289,8 +298,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   bf16x8 pb[BN / 16];
   score_tile<D, BN>(s, Kbuf0, qb, lc, lg);
   if (masked(0)) mask_tile<BN>(s, 0, qlim, lg);
-  softmax_max<D, BN>(s, m_run, l_run, oacc, scale_log2);
-  softmax_exp<BN>(s, pb, m_run, l_run, scale_log2);
+  softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
 
   // The two waves on each SIMD (waves w and w + 4) alternate: group 1 runs
   // one barrier interval behind group 0, so while one issues the step's
@@ -313,8 +321,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // tensor and fetch tile t+3.
     if (t + 1 < num_kt) {
       if (masked(t + 1)) mask_tile<BN>(s, (t + 1) * BN, qlim, lg);
-      softmax_max<D, BN>(s, m_run, l_run, oacc, scale_log2);
-      softmax_exp<BN>(s, pb, m_run, l_run, scale_log2);
+      softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     }
     if (t + 2 < num_kt) {
       store_tile<D, BN, 256>(stage, (t & 1) ? mybuf1 : mybuf0, group == 0 ? C::kKPitch : C::kVPitch, gtid);
