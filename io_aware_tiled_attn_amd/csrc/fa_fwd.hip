@@ -209,6 +209,9 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x
   };
 #pragma unroll
   for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
+  // The matrix wave takes issue priority over the SIMD's other wave (in its
+  // vector phase), so MFMAs are not held back behind its exponentials.
+  __builtin_amdgcn_s_setprio(1);
   bf16x8 ring[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) ring[i] = load(i);
@@ -226,6 +229,7 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x
     if (i + L < kAll) ring[i % L] = load(i + L);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, int BN, bool CAUSAL>
