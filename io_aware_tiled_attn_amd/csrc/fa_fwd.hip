@@ -13,19 +13,20 @@
 //     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so the
 //     32x32 accumulator puts one query per lane column: the row max and row
 //     sum are in-lane reductions plus one permlane32 swap.
-//   * K and V tiles of BN keys are staged in LDS (double buffered) and
-//     shared by the 8 waves.  Each key-tile step has two barrier-separated
+//   * K and V tiles of BN keys are copied into LDS (three buffers each)
+//     straight from global memory (buffer_load ... lds: no registers and no
+//     LDS write instructions) and shared by the 8 waves.  Each key-tile step has two barrier-separated
 //     phases: a matrix phase (O += P(t) V(t) and S(t+1) = K(t+1) Q^T) and a
 //     vector phase (the online softmax of S(t+1)).  Waves 4-7 run one phase
 //     behind waves 0-3, so the two waves sharing a SIMD alternate between the
-//     matrix cores and the vector ALU.  Waves 0-3 stage the K tiles and waves
-//     4-7 the V tiles, each in its own vector phase.
-//   * K and V are stored row-major with padding.  The A operand of
-//     O^T += V^T P^T (V transposed) is read with ds_read_b64_tr_b16, which
-//     hands each lane four consecutive keys of one feature column; the two
-//     reads per operand take the key order the S^T accumulator leaves in each
-//     lane.  V's row pitch (d + 32 elements) puts the four rows read by each
-//     16-lane group, and the two groups of a half-wave, on disjoint banks.
+//     matrix cores and the vector ALU.  Waves 0-3 copy the K tiles and waves
+//     4-7 the V tiles.
+//   * K and V are stored row-major, rows unpadded, with the 16-byte chunks
+//     of each row XOR-permuted so both products read conflict-free.  The A
+//     operand of O^T += V^T P^T (V transposed) is read with
+//     ds_read_b64_tr_b16, which hands each lane four consecutive keys of one
+//     feature column; the two reads per operand take the key order the S^T
+//     accumulator leaves in each lane.
 //   * P is rounded to bf16 (RNE) and fed back as the B operand directly from
 //     the accumulator registers; O^T accumulates in fp32.
 //   * The running reference m is the first tile's max and is raised only
@@ -53,66 +54,84 @@ struct FwdCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int BM = kWaves * 32;
-  static constexpr int kKPitch = D + 8;    // bf16 elements per K row in LDS
-  static constexpr int kVPitch = D + 32;   // bf16 elements per V row in LDS
-  static constexpr int kKTile = BN * kKPitch;
-  static constexpr int kVTile = BN * kVPitch;
-  // LDS: K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1
-  static constexpr int kLdsBytes = 2 * (kKTile + kVTile) * 2;
-  static constexpr int kChunks = BN * D / 8;              // 16-byte chunks per tile
-  static constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
+  static constexpr int kTile = BN * D;     // bf16 elements per K or V tile (unpadded rows)
+  static constexpr int kBufs = 3;          // LDS buffers per tensor
+  // LDS: K buffers 0..2 | V buffers 0..2
+  static constexpr int kLdsBytes = 2 * kBufs * kTile * 2;
+  // Each group of four waves copies one tensor; 1 KB per copy instruction.
+  static constexpr int kDmaPerWave = kTile * 2 / 1024 / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(kDmaPerWave >= 1 && kTile * 2 % 4096 == 0, "tile must split into 1 KB copies per wave");
   static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
 };
 
-template <int D, int BN, int THREADS>
-struct TileStage {
-  static constexpr int kChunks = BN * D / 8;              // 16-byte chunks per tile
-  static constexpr int kPer = (kChunks + THREADS - 1) / THREADS;
-  u32x4 c[kPer];
+// Tiles sit in LDS with unpadded rows; the 16-byte chunks of each row are
+// permuted (chunk c of row r is stored at chunk c ^ f(r)) so that the reads
+// of both products hit 64 distinct banks:
+//   * K, read as MFMA A operands (16 lanes = 16 consecutive rows at one
+//     chunk): f spreads 16 consecutive rows over all chunk positions.
+//   * V, read with ds_read_b64_tr_b16 (a half-wave covers 4 consecutive
+//     rows x 4 consecutive chunks): f moves each of 4 consecutive rows to
+//     a different group of 4 chunks.
+// Rows per 256-byte bank sweep: 1 for d = 128, 2 for d = 64.
+template <int D>
+struct Swizzle {
+  static constexpr int kCpr = D / 8;     // chunks per row
+  static constexpr int kRpb = 128 / D;   // rows per bank sweep
+  __device__ static int k(int r) { return (r / kRpb) % kCpr; }
+  __device__ static int v(int r) { return 4 * ((r / kRpb) % (kCpr / 4)); }
 };
 
-// Global -> registers: this thread's 16-byte chunks of a BN x D tile (rows
-// past the head's end read as zero through the buffer descriptor).
-template <int D, int BN, int THREADS>
-__device__ __forceinline__ void load_tile(TileStage<D, BN, THREADS>& st, __amdgpu_buffer_rsrc_t r, int j0, int tid) {
-  using S = TileStage<D, BN, THREADS>;
+// One buffer_load_dwordx4 ... lds: each lane's 16 bytes at byte offset goff
+// of the buffer go to LDS address lds_addr + 16 * lane (lds_addr is uniform
+// and travels in M0).  Written as inline assembly so that the compiler does
+// not guard every later LDS read of this wave with a wait for the copy (it
+// cannot tell which LDS bytes the copy writes); the kernel orders the copy
+// itself, with an explicit vmcnt wait and a barrier before any read of the
+// bytes it fills.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t goff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(goff), "s"(r), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// Global -> LDS without registers (buffer_load ... lds): this wave's share
+// of a BN x D tile starting at key j0.  Each instruction fills 1 KB of LDS
+// in lane order (lane i writes bytes 16i..16i+15); lane i therefore loads
+// the global chunk that the swizzle stores at that position.  Rows past the
+// head's end read as zero through the buffer descriptor.  Completion is
+// tracked by this wave's vmcnt.
+template <int D, int BN, bool IS_K>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile, int j0, int wq, int lane) {
+  using C = FwdCfg<D, BN>;
+  using Z = Swizzle<D>;
+  constexpr int kRowsPerInst = 1024 / (2 * D);
 #pragma unroll
-  for (int i = 0; i < S::kPer; ++i) {
-    const int c = tid + i * THREADS;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    if (S::kChunks % THREADS == 0 || c < S::kChunks) st.c[i] = bload128(r, (uint32_t)((j0 + row) * D + col) * 2u);
+  for (int i = 0; i < C::kDmaPerWave; ++i) {
+    const int inst = wq * C::kDmaPerWave + i;
+    const int row = inst * kRowsPerInst + lane / Z::kCpr;
+    const int chunk = (lane % Z::kCpr) ^ (IS_K ? Z::k(row) : Z::v(row));
+    const uint32_t goff = (uint32_t)((j0 + row) * D + 8 * chunk) * 2u;
+    lds_copy16(r, goff, (uint32_t)(uintptr_t)(tile + inst * 512));
   }
 }
 
-// Registers -> LDS, row-major with `pitch` elements per row.
-template <int D, int BN, int THREADS>
-__device__ __forceinline__ void store_tile(const TileStage<D, BN, THREADS>& st, __bf16* S, int pitch, int tid) {
-  using T = TileStage<D, BN, THREADS>;
-#pragma unroll
-  for (int i = 0; i < T::kPer; ++i) {
-    const int c = tid + i * THREADS;
-    if (T::kChunks % THREADS == 0 || c < T::kChunks) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)(S + row * pitch + col) = st.c[i];
-    }
-  }
-}
+// s_waitcnt vmcnt(0), leaving the other counters alone.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // S^T = K Q^T for one tile: BN keys x this wave's 32 queries.  The k-steps
 // run outermost so the BN/32 accumulator chains interleave.
+// koff[ks] is this lane's element offset of its A operand for k-step ks
+// (row lc, chunk 2 ks + lg, swizzled); 32-row blocks add 32 D.
 template <int D, int BN>
-__device__ __forceinline__ void score_tile(f32x16 (&s)[BN / 32], const __bf16* Ks, const bf16x8 (&qb)[D / 16],
-                                          int lc, int lg) {
-  using C = FwdCfg<D, BN>;
+__device__ __forceinline__ void score_tile(f32x16 (&s)[BN / 32], const __bf16* Ks, const int (&koff)[D / 16],
+                                          const bf16x8 (&qb)[D / 16]) {
 #pragma unroll
   for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
-  const __bf16* krow = Ks + lc * C::kKPitch + 8 * lg;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
     for (int mb = 0; mb < BN / 32; ++mb) {
-      const bf16x8 a = *(const bf16x8*)(krow + 32 * mb * C::kKPitch + 16 * ks);
+      const bf16x8 a = *(const bf16x8*)(Ks + koff[ks] + 32 * mb * D);
       s[mb] = mfma32(a, qb[ks], s[mb]);
     }
 }
@@ -186,26 +205,25 @@ __device__ __forceinline__ void softmax_step(const f32x16 (&s)[BN / 32], bf16x8 
 }
 
 // Both products of a matrix phase, O += P(t) V(t) then S(t+1) = K(t+1) Q^T,
-// as one stream of MFMAs whose LDS operands are read kLookahead products
-// ahead, so the read latency hides behind the preceding MFMAs instead of
-// stalling each one.  Scheduling barriers keep the stream in this order.
+// as one stream of MFMAs whose LDS operands are read L products ahead, so
+// the read latency hides behind the preceding MFMAs instead of stalling
+// each one.  Scheduling barriers keep the stream in this order.  voff[dm]
+// is this lane's element offset of its V^T operand reads for feature block
+// dm (swizzled); 16-key steps add 16 D.
 template <int D, int BN, int L>
 __device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vs,
-                                             int v_lane_off, f32x16 (&s)[BN / 32], const __bf16* Ks,
-                                             const bf16x8 (&qb)[D / 16], int lc, int lg) {
-  using C = FwdCfg<D, BN>;
+                                             const int (&voff)[D / 32], f32x16 (&s)[BN / 32], const __bf16* Ks,
+                                             const int (&koff)[D / 16], const bf16x8 (&qb)[D / 16]) {
   constexpr int kPv = BN / 16 * (D / 32);   // O += P V products
   constexpr int kS = D / 16 * (BN / 32);    // S = K Q^T products
   constexpr int kAll = kPv + kS;
-  const __bf16* vp = Vs + v_lane_off;
-  const __bf16* krow = Ks + lc * C::kKPitch + 8 * lg;
   auto load = [&](int i) -> bf16x8 {
     if (i < kPv) {
       const int c = i / (D / 32), dm = i % (D / 32);
-      return lds_tr_pair(vp, (16 * c) * C::kVPitch + 32 * dm, (16 * c + 8) * C::kVPitch + 32 * dm);
+      return lds_tr_pair(Vs + voff[dm], (16 * c) * D, (16 * c + 8) * D);
     }
     const int j = i - kPv, ks = j / (BN / 32), mb = j % (BN / 32);
-    return *(const bf16x8*)(krow + 32 * mb * C::kKPitch + 16 * ks);
+    return *(const bf16x8*)(Ks + koff[ks] + 32 * mb * D);
   };
 #pragma unroll
   for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
@@ -246,7 +264,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63;
   const int lc = lane & 31;      // lane column: query within the wave
   const int lg = lane >> 5;      // lane half
-  const int gtid = tid & 255;    // thread index within the group
+  const int wq = wave & 3;       // wave within its group
 
   const int bid = blockIdx.x;
   const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
@@ -254,15 +272,31 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
-  // Group 0 stages the K tiles, group 1 the V tiles.
+  // Group 0 copies the K tiles into LDS, group 1 the V tiles.
   const __amdgpu_buffer_rsrc_t rmine = make_rsrc((group == 0 ? K : V) + head_off, head_bytes);
-  __bf16* Kbuf0 = smem;
-  __bf16* Kbuf1 = smem + C::kKTile;
-  __bf16* Vbuf0 = smem + 2 * C::kKTile;
-  __bf16* Vbuf1 = smem + 2 * C::kKTile + C::kVTile;
-  __bf16* mybuf0 = group == 0 ? Kbuf0 : Vbuf0;
-  __bf16* mybuf1 = group == 0 ? Kbuf1 : Vbuf1;
-  const int v_lane_off = tr_lane_off(lane, C::kVPitch, 4);
+  auto kbuf = [&](int i) { return smem + i * C::kTile; };
+  auto vbuf = [&](int i) { return smem + (C::kBufs + i) * C::kTile; };
+  auto copy_tile = [&](int tile, int buf) {
+    if (group == 0) dma_tile<D, BN, true>(rmine, kbuf(buf), tile * BN, wq, lane);
+    else dma_tile<D, BN, false>(rmine, vbuf(buf), tile * BN, wq, lane);
+  };
+
+  // This lane's swizzled LDS offsets.  K (A operand of S^T = K Q^T): row lc,
+  // chunk 2 ks + lg.  V (A operand of O^T += V^T P^T via the transposing
+  // read): lane (s = lane % 16, G = bit 4, g = bit 5) reads row 4 g + s / 4
+  // of each 8-row group at column 32 dm + 16 G + 4 (s % 4); f(row) depends
+  // only on s / 4 because the group offsets are multiples of 8 rows.
+  using Z = Swizzle<D>;
+  int koff[D / 16], voff[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lc * D + 8 * ((2 * ks + lg) ^ Z::k(lc));
+  {
+    const int sl = lane & 15, G = (lane >> 4) & 1;
+    const int row = 4 * lg + (sl >> 2);
+#pragma unroll
+    for (int dm = 0; dm < D / 32; ++dm)
+      voff[dm] = row * D + 8 * ((4 * dm + 2 * G + ((sl & 3) >> 1)) ^ Z::v(row)) + 4 * (sl & 1);
+  }
 
   const int q_wave0 = qt * C::BM + wave * 32;
   const int q_idx = q_wave0 + lc;
@@ -285,22 +319,16 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
   auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
-  // Each group stages tiles 0 and 1 of its tensor, and holds tile 2 in
-  // registers until its first write slot.
-  TileStage<D, BN, 256> stage;
-  load_tile<D, BN, 256>(stage, rmine, 0, gtid);
-  store_tile<D, BN, 256>(stage, mybuf0, group == 0 ? C::kKPitch : C::kVPitch, gtid);
-  if (num_kt > 1) {
-    load_tile<D, BN, 256>(stage, rmine, BN, gtid);
-    store_tile<D, BN, 256>(stage, mybuf1, group == 0 ? C::kKPitch : C::kVPitch, gtid);
-  }
-  if (num_kt > 2) load_tile<D, BN, 256>(stage, rmine, 2 * BN, gtid);
+  // Tiles 0 and 1 of each tensor.  Tile t lives in buffer t % 3.
+  copy_tile(0, 0);
+  if (num_kt > 1) copy_tile(1, 1);
+  wait_vmem_all();
   __syncthreads();
 
   // S(0) and P(0).
   f32x16 s[BN / 32];
   bf16x8 pb[BN / 16];
-  score_tile<D, BN>(s, Kbuf0, qb, lc, lg);
+  score_tile<D, BN>(s, kbuf(0), koff, qb);
   if (masked(0)) mask_tile<BN>(s, 0, qlim, lg);
   softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
 
@@ -308,30 +336,33 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // one barrier interval behind group 0, so while one issues the step's
   // MFMAs the other is in its exponentials.  Every wave passes the same
   // number of barriers (group 1 one extra here, group 0 one extra at the
-  // end).  Buffer t % 2 holds tile t; a tile's buffer is rewritten only in
-  // the interval after both groups' last read of the tile it held.
+  // end).  At the start of its matrix phase of step t each group starts the
+  // copy of tile t+2 of its tensor into buffer (t+2) % 3, and waits for it
+  // at the end of its vector phase of the same step.  That buffer's previous
+  // tile (t-1) was last read at least one barrier before the copy starts,
+  // and the new tile is first read at least one barrier after the wait.
   if (group == 1) __syncthreads();
 
+  int b_cur = 0;   // t % 3
   for (int t = 0; t < num_kt; ++t) {
+    const int b_next = b_cur == 2 ? 0 : b_cur + 1;    // (t + 1) % 3
+    const int b_copy = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
+    if (t + 2 < num_kt) copy_tile(t + 2, b_copy);
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
     // wave runs the same instruction stream on every step: on causal tiles
     // wholly above a wave's queries its P is all zero (the tile is masked
     // like any other), and on the last step the score product reads a stale
     // buffer and its result is not used.
-    matrix_phase<D, BN, FWD_LOOKAHEAD>(oacc, pb, (t & 1) ? Vbuf1 : Vbuf0, v_lane_off, s,
-                                       ((t + 1) & 1) ? Kbuf1 : Kbuf0, qb, lc, lg);
+    matrix_phase<D, BN, FWD_LOOKAHEAD>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
-    // Phase 2 (vector ALU): P(t+1); publish tile t+2 of this group's
-    // tensor and fetch tile t+3.
+    // Phase 2 (vector ALU): P(t+1).
     if (t + 1 < num_kt) {
       if (masked(t + 1)) mask_tile<BN>(s, (t + 1) * BN, qlim, lg);
       softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     }
-    if (t + 2 < num_kt) {
-      store_tile<D, BN, 256>(stage, (t & 1) ? mybuf1 : mybuf0, group == 0 ? C::kKPitch : C::kVPitch, gtid);
-      if (t + 3 < num_kt) load_tile<D, BN, 256>(stage, rmine, (t + 3) * BN, gtid);
-    }
+    wait_vmem_all();
     __syncthreads();
+    b_cur = b_next;
   }
   if (group == 0) __syncthreads();
 
