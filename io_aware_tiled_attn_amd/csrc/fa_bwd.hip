@@ -158,8 +158,8 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // uniform per wave
   const int lane = tid & 63;
   const int lc = lane & 31, lg = lane >> 5;
-  const int kt = blockIdx.x / BH;       // key tile; small kt = most query tiles
-  const int bh = blockIdx.x % BH;
+  int kt, bh;   // key tile (small kt = most query tiles) and head
+  xcd_head_major(blockIdx.x, BH, (N + C::BN - 1) / C::BN, bh, kt);
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   BwdHead h;

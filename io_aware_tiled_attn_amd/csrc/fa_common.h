@@ -109,4 +109,23 @@ __device__ __forceinline__ void batomic_add(__amdgpu_buffer_rsrc_t r, uint32_t o
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)off, 0, 0);
 }
 
+// Work order for a launch of num_tiles x BH workgroups (tile-major work
+// items of BH heads).  The dispatcher hands workgroup i to XCD i % 8, and
+// each XCD has its own L2.  When BH is a multiple of 8, XCD x takes heads
+// x, x + 8, ... one after another, all tiles of a head before the next
+// head, tile 0 first: the tiles running together on an XCD then share one
+// or two heads' K/V (forward) or dQ accumulator (backward) in its L2.
+// Otherwise workgroups take tiles in order with the head index varying
+// fastest.
+__device__ __forceinline__ void xcd_head_major(int bid, int BH, int num_tiles, int& bh, int& tile) {
+  if ((BH & 7) == 0) {
+    const int j = bid >> 3;
+    tile = j % num_tiles;
+    bh = (j / num_tiles) * 8 + (bid & 7);
+  } else {
+    tile = bid / BH;
+    bh = bid % BH;
+  }
+}
+
 }  // namespace fa

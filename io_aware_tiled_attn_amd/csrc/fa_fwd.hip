@@ -38,7 +38,9 @@
 //     last row return zeros, so ragged tails need no branches.
 //   * Workgroups are issued heaviest first (causal), with all query tiles of
 //     one head on the same XCD (dispatch is round-robin over 8 XCDs and the
-//     head index is the fast-varying part of the workgroup id).
+//     head index is the fast-varying part of the workgroup id).  Keeping the
+//     global heaviest-first order beats working through one head at a time
+//     per XCD, even though the latter reads K and V from memory only once.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -403,7 +405,7 @@ fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
   const int tid = threadIdx.x;
   const int part = tid % TPQ;
   const int bid = blockIdx.x;
-  const int qt = num_qt - 1 - bid / BH;
+  const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
   const int bh = bid % BH;
   const int q_idx = qt * QPB + tid / TPQ;
   const size_t head_off = (size_t)bh * N * D;
