@@ -230,7 +230,8 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     //   S = Q K^T and dP = dO V^T (32 queries x this wave's 32 keys);
     //   P = exp2(s * scale * log2 e - LSE * log2 e), dS = P (dP - D), each
     //   kept as a bf16 pair (rounded value, rounded residual), with causal
-    //   masking (key > query) and keys past N giving P = 0; dS^T to LDS;
+    //   masking (key > query) and keys past N giving P = 0 (scores set to
+    //   -inf, on the steps that need it); dS^T to LDS;
     //   dV^T += dO^T P and dK^T += Q^T dS, the A operands read down the
     //   columns in the key order P's accumulator layout leaves in each lane.
     // With one wave per SIMD, the matrix and vector work of the two blocks
@@ -239,6 +240,9 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     // MFMAs beside block 1's vector work; scheduling barriers keep the
     // chunks in order.
     static_assert(QB == 2, "the step interleaves exactly two query blocks");
+    // Masking is needed only where this wave's keys run past N or (causal)
+    // past the step's first query; elsewhere every P is kept.
+    const bool step_mask = (kw0 + 31 >= N) || (CAUSAL && q0 < kw0 + 31);
     const __bf16* qrow = Qs + row_lane_off;
     const __bf16* grow = Gs + row_lane_off;
     const __bf16* gtr = Gs + tr_off_p;
@@ -249,6 +253,17 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     constexpr int UPC = (2 * DM + 3) / 4;      // (c, dm) dV/dK pairs per chunk
 
     f32x16 sc[QB], dpc[QB];
+    // Scores of masked (key, query) pairs to -inf, so P and dS are 0 there.
+    auto mask_scores = [&](int b) {
+      if (step_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + 32 * b + 8 * (r >> 2) + 4 * lg + (r & 3);
+          const bool keep = key_ok & (!CAUSAL | (q >= key));
+          sc[b][r] = keep ? sc[b][r] : -INFINITY;
+        }
+      }
+    };
     auto score_steps = [&](int b, int ks0, int ks1) {
 #pragma unroll
       for (int ks = ks0; ks < ks1; ++ks) {
@@ -261,7 +276,6 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     };
     uint32_t pw[QB][8], pl[QB][8], dsw[QB][8], dsl[QB][8];
     auto vector_group = [&](int b, int i) {
-      const int qb0 = q0 + 32 * b;
       const f32x4 l4 = *(const f32x4*)(Ls + 32 * b + 8 * i + 4 * lg);
       const f32x4 d4 = *(const f32x4*)(Ds + 32 * b + 8 * i + 4 * lg);
       float p[4], ds[4];
@@ -269,9 +283,7 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * i + j;
         const float pe = fast_exp2(__builtin_fmaf(sc[b][r], scale_log2, -l4[j]));
-        const int q = qb0 + 8 * i + 4 * lg + j;
-        const bool keep = key_ok & (!CAUSAL | (q >= key));
-        const float pv = keep ? pe : 0.f;
+        const float pv = pe;
         p[j] = pv;
         ds[j] = pv * (dpc[b][r] - d4[j]);
       }
@@ -313,6 +325,7 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
       dpc[b] = (f32x16){};
     }
     score_steps(0, 0, KS);
+    mask_scores(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -320,6 +333,8 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
       vector_group(0, j);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mask_scores(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       update_pairs(0, min(2 * DM, j * UPC), min(2 * DM, (j + 1) * UPC));
