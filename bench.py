@@ -100,6 +100,18 @@ def cpu_baseline(w, inp, gpu_out, heads):
             errs[name] = max(errs[name], float(np.max(np.abs(gpu_out[name][b, h] - ref))))
     f_fwd, f_bwd = flops(w)
     per_head = (f_fwd + f_bwd) / (w.B * w.H)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({"%s %s" % (p.get("internal_api", "?"), p.get("version", "")) for p in threadpool_info()}))
+    except Exception:
+        pass
     return {
         "value": per_head * len(picks) / elapsed / 1e12,
         "unit": "TFLOP/s",
@@ -109,6 +121,10 @@ def cpu_baseline(w, inp, gpu_out, heads):
                   f"({elapsed:.1f} s); FLOPs counted with the GPU's convention (the oracle itself forms the "
                   f"full masked N x N matrices)",
         "seconds": elapsed,
+        "cpu": cpu_model,
+        "blas": blas,
+        # the oracle forms the full masked N x N matrices: 4 N^2 d FLOP forward, 2.5x that backward
+        "oracle_gflops_dense": round(4.0 * w.N * w.N * w.d * 3.5 * len(picks) / elapsed / 1e9, 2),
     }, errs
 
 
@@ -182,10 +198,12 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    fin_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+    per_kernel = {name: np.array([e[i].elapsed_time(e[i + 1]) for e in events])
+                  for i, name in enumerate(("forward", "preprocess", "main", "finalize"))}
+    fwd_ms, prep_ms, main_ms, fin_ms = (float(per_kernel[n].mean()) for n in per_kernel)
+    kernel_stats = {n: {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+                        "min": round(float(a.min()), 4), "max": round(float(a.max()), 4),
+                        "std": round(float(a.std()), 4)} for n, a in per_kernel.items()}
 
     f_fwd, f_bwd = flops(w)
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
@@ -229,6 +247,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        "kernel_ms": kernel_stats,
         "peak_basis": "MI355X dense bf16 MFMA 2.5 PFLOP/s (published); FLOPs: fwd 4BHN^2d (x1/2 causal), "
                       "bwd 2.5x fwd",
     }
