@@ -26,6 +26,13 @@ Readings where the pages are silent:
   * LSE: the per-row log-sum-exp of the scaled, masked scores, natural log:
     LSE_i = m_i + ln(l_i).  A row with every key masked (impossible for
     causal with N_q = N_k, kept for completeness) gets O = 0, LSE = -inf.
+  * block-sparse attention: the pages name block-sparse FlashAttention as
+    an approximate extension (chorfi.xyz, "Main concepts to understand"; its
+    Path-256 result in vibeengines.com's table of headline numbers) without
+    defining it.  Reading: a block mask over (query block, key block) pairs;
+    the scores of every pair whose mask entry is 0 are -inf (weight 0), the
+    rest is ordinary attention.  Rows left with no key get O = 0, LSE = -inf
+    and zero gradients.
   * backward: the pages only say the backward pass recomputes attention
     instead of storing it (chorfi.xyz "Study objectives"; modelfieldguide.com
     "An IO-aware rewrite").  The gradients below are the calculus of the
@@ -75,11 +82,23 @@ def _causal_mask(row_idx, n_keys):
     return j > np.asarray(row_idx)[:, None]
 
 
-def attention_forward_head(q, k, v, scale=None, causal=False, rows=None):
+def _block_masked(row_idx, n_keys, block_mask, block):
+    """True where (query row, key) falls in a (query block, key block) pair
+    whose block-mask entry is 0."""
+    bq, bk = block
+    bm = np.asarray(block_mask) != 0
+    qb = np.asarray(row_idx) // bq
+    kb = np.arange(n_keys) // bk
+    return ~bm[qb][:, kb]
+
+
+def attention_forward_head(q, k, v, scale=None, causal=False, rows=None, block_mask=None, block=(128, 128)):
     """Exact attention for one head.
 
     q: [Nq, d], k: [Nk, d], v: [Nk, dv], any real dtype (promoted to float64).
     rows: optional index array of query rows to evaluate (default: all).
+    block_mask: optional [ceil(Nq/bq), ceil(Nk/bk)] array for block-sparse
+    attention, block = (bq, bk); pairs whose entry is 0 are masked.
     Returns (O [len(rows), dv], LSE [len(rows)]) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -98,6 +117,8 @@ def attention_forward_head(q, k, v, scale=None, causal=False, rows=None):
         s = scale * (q[r] @ k.T)                       # scores, [rows, Nk]
         if causal:
             s[_causal_mask(r, n_keys)] = -np.inf
+        if block_mask is not None:
+            s[_block_masked(r, n_keys, block_mask, block)] = -np.inf
         m = np.max(s, axis=1)                          # row max
         live = m > -np.inf
         m_safe = np.where(live, m, 0.0)
@@ -110,9 +131,10 @@ def attention_forward_head(q, k, v, scale=None, causal=False, rows=None):
     return out, lse
 
 
-def attention_forward(q, k, v, scale=None, causal=False):
+def attention_forward(q, k, v, scale=None, causal=False, block_mask=None, block=(128, 128)):
     """Exact attention over [B, H, N, d] arrays; returns (O, LSE) float64
-    with shapes [B, H, N, dv] and [B, H, N]."""
+    with shapes [B, H, N, dv] and [B, H, N].  block_mask, if given, is
+    [B, H, ceil(N/bq), ceil(N/bk)]."""
     q = np.asarray(q)
     B, H, N, _ = q.shape
     out = np.zeros((B, H, N, v.shape[-1]), dtype=np.float64)
@@ -120,14 +142,16 @@ def attention_forward(q, k, v, scale=None, causal=False):
     for b in range(B):
         for h in range(H):
             out[b, h], lse[b, h] = attention_forward_head(
-                q[b, h], k[b, h], v[b, h], scale=scale, causal=causal)
+                q[b, h], k[b, h], v[b, h], scale=scale, causal=causal,
+                block_mask=None if block_mask is None else block_mask[b, h], block=block)
     return out, lse
 
 
-def attention_backward_head(q, k, v, do, scale=None, causal=False):
+def attention_backward_head(q, k, v, do, scale=None, causal=False, block_mask=None, block=(128, 128)):
     """Analytic gradients of O = softmax(scale * q k^T [masked]) v for one head.
 
-    q: [N, d], k: [N, d], v: [N, dv], do: [N, dv].
+    q: [N, d], k: [N, d], v: [N, dv], do: [N, dv]; block_mask as in
+    attention_forward_head.
     Returns (dq, dk, dv, D) in float64, where D_i = sum_k dO_ik O_ik.
     The N x N matrices are formed whole; callers keep N moderate.
     """
@@ -141,6 +165,8 @@ def attention_backward_head(q, k, v, do, scale=None, causal=False):
     s = scale * (q @ k.T)
     if causal:
         s[_causal_mask(np.arange(n_q), n_k)] = -np.inf
+    if block_mask is not None:
+        s[_block_masked(np.arange(n_q), n_k, block_mask, block)] = -np.inf
     m = np.max(s, axis=1)
     live = m > -np.inf
     m_safe = np.where(live, m, 0.0)
@@ -158,7 +184,7 @@ def attention_backward_head(q, k, v, do, scale=None, causal=False):
     return dq, dk, dv, D
 
 
-def attention_backward(q, k, v, do, scale=None, causal=False):
+def attention_backward(q, k, v, do, scale=None, causal=False, block_mask=None, block=(128, 128)):
     """Analytic gradients over [B, H, N, d] arrays; returns (dQ, dK, dV)."""
     B, H, N, d = np.asarray(q).shape
     dq = np.zeros((B, H, N, d), dtype=np.float64)
@@ -167,5 +193,6 @@ def attention_backward(q, k, v, do, scale=None, causal=False):
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h], _ = attention_backward_head(
-                q[b, h], k[b, h], v[b, h], do[b, h], scale=scale, causal=causal)
+                q[b, h], k[b, h], v[b, h], do[b, h], scale=scale, causal=causal,
+                block_mask=None if block_mask is None else block_mask[b, h], block=block)
     return dq, dk, dv

@@ -39,6 +39,10 @@ MUTANTS = {
     "bwd_dp_wrong_operand": ("dp = do @ v.T", "dp = do @ q.T"),
     "bwd_mask_dropped": ("        s[_causal_mask(np.arange(n_q), n_k)] = -np.inf",
                          "        pass"),
+    "block_mask_transposed": ("    return ~bm[qb][:, kb]", "    return ~bm.T[qb][:, kb]"),
+    "block_rows_use_key_block_size": ("    qb = np.asarray(row_idx) // bq", "    qb = np.asarray(row_idx) // bk"),
+    "bwd_block_mask_dropped": ("        s[_block_masked(np.arange(n_q), n_k, block_mask, block)] = -np.inf",
+                               "        pass"),
 }
 
 
@@ -114,6 +118,33 @@ def _battery(mod):
                 and np.allclose(dk, tk.grad[0, 0].numpy(), atol=1e-12)
                 and np.allclose(dv, tv.grad[0, 0].numpy(), atol=1e-12)):
             failed.append(f"autograd_{causal}")
+    # Block mask (non-square blocks, non-symmetric mask): forward against
+    # scalar loops, backward against torch autograd with the element mask.
+    n, bq, bk = 9, 2, 3
+    mask = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 0], [0, 0, 1], [1, 0, 0]], dtype=np.uint8)
+    allowed = mask[np.arange(n)[:, None] // bq, np.arange(n)[None, :] // bk] != 0
+    q, k, v, do = (rng.standard_normal((n, 3)) for _ in range(4))
+    try:
+        o, lse = mod.attention_forward_head(q, k, v, scale=0.6, block_mask=mask, block=(bq, bk))
+        bo = np.zeros((n, 3)); bl = np.zeros(n)
+        for i in range(n):
+            js = [j for j in range(n) if allowed[i, j]]
+            sc = [0.6 * sum(a * b for a, b in zip(q[i], k[j])) for j in js]
+            m = max(sc); tot = sum(math.exp(x - m) for x in sc)
+            bo[i] = sum(math.exp(x - m) / tot * v[j] for x, j in zip(sc, js))
+            bl[i] = m + math.log(tot)
+        if not (np.allclose(o, bo, atol=1e-12) and np.allclose(lse, bl, atol=1e-12)):
+            failed.append("block_brute")
+        dq, dk, dv, _ = mod.attention_backward_head(q, k, v, do, scale=0.6, block_mask=mask, block=(bq, bk))
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(allowed),
+                                                              scale=0.6)
+        to.backward(torch.from_numpy(do))
+        if not (np.allclose(dq, tq.grad.numpy(), atol=1e-12) and np.allclose(dk, tk.grad.numpy(), atol=1e-12)
+                and np.allclose(dv, tv.grad.numpy(), atol=1e-12)):
+            failed.append("block_autograd")
+    except Exception:
+        failed.append("block_raised")
     return failed
 
 
