@@ -42,6 +42,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-blocksparse", action="store_true",
+                    help="skip the block-sparse step reported beside the dense one")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB once (device to device) so that "
                          "HBM byte counters can be scaled against a transfer of known size")
@@ -126,6 +128,63 @@ def cpu_baseline(w, inp, gpu_out, heads):
         # the oracle forms the full masked N x N matrices: 4 N^2 d FLOP forward, 2.5x that backward
         "oracle_gflops_dense": round(4.0 * w.N * w.N * w.d * 3.5 * len(picks) / elapsed / 1e9, 2),
     }, errs
+
+
+def blocksparse_step(q, k, v, do, o, lse, dq, dk, dv, ws, stream, dense_ms, warmup, steps):
+    """The block-sparse workload (same shape, the local-band + global-column
+    block mask, non-causal), forward + backward on the same tensors.  FLOPs
+    are counted on the kept (128 x 128) blocks only, with the dense
+    convention (forward 4 d per kept query-key pair, backward 2.5x)."""
+    import numpy as np
+    import torch
+    import io_aware_tiled_attn_amd as fa
+    from io_aware_tiled_attn_amd import workloads as wl
+    w = wl.SPARSE_WORKLOAD
+    B, H, N, d = q.shape
+    mask_np = wl.local_global_block_mask(B, H, N)
+    mask = torch.from_numpy(mask_np).cuda()
+    kept = int(mask_np.astype(np.int64).sum())
+    f_fwd = 4.0 * d * kept * wl.SPARSE_BLOCK * wl.SPARSE_BLOCK
+    f_bwd = 2.5 * f_fwd
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.flash_attn_fwd_blocksparse(q, k, v, mask, out=o, lse=lse)
+        if ev:
+            ev[1].record(stream)
+        fa.flash_attn_bwd_blocksparse(q, k, v, o, lse, do, mask, workspace=ws, dq=dq, dk=dk, dv=dv)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    tf = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+    return {
+        "workload": "%s: B=%d H=%d N=%d d=%d bf16, non-causal, block mask local band 2 + global first key "
+                    "block (128 x 128 blocks), same tensors as the dense step" % (w.name, B, H, N, d),
+        "kept_block_fraction": round(kept / mask_np.size, 4),
+        "ms_per_step": round(ms, 4),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "tflops": round(tf, 2),
+        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "unit": "TFLOP/s on kept blocks",
+        "speedup_vs_dense_causal_step": round(dense_ms / ms, 3),
+    }
 
 
 def main():
@@ -251,6 +310,10 @@ def main():
         "peak_basis": "MI355X dense bf16 MFMA 2.5 PFLOP/s (published); FLOPs: fwd 4BHN^2d (x1/2 causal), "
                       "bwd 2.5x fwd",
     }
+    if not args.no_blocksparse:
+        print("[bench] block-sparse step", file=sys.stderr, flush=True)
+        result["blocksparse"] = blocksparse_step(q, k, v, do, o, lse, dq, dk, dv, ws, stream, ms_per_step,
+                                                 max(5, args.warmup // 2), max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         gpu_out = {"o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.float().cpu().numpy(),

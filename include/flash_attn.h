@@ -163,6 +163,44 @@ int flash_attn_bwd_ex(const void* q, const void* k, const void* v,
                       float scale, int causal, int dtype, void* stream,
                       int phases);
 
+/*
+ * Block-sparse attention.  The pages name block-sparse FlashAttention as an
+ * approximate extension of the method (chorfi.xyz study guide, "Main
+ * concepts to understand"; vibeengines.com lists its Path-256 result among
+ * the headline numbers) without defining it.  Here: a block mask over
+ * (query block, key block) pairs of FA_SPARSE_BLOCK x FA_SPARSE_BLOCK
+ * elements; the scores of every pair whose mask entry is 0 are -inf (weight
+ * 0), and the rest is the attention defined above (with the causal mask on
+ * top when causal = 1).  A query row left with no key gets O = 0,
+ * LSE = -inf, and zero gradients.
+ *   block_mask : device pointer to unsigned char [B, H, nb, nb],
+ *                nb = ceil(N / FA_SPARSE_BLOCK); entry [b][h][i][j] != 0
+ *                keeps the pair (query block i, key block j).  Read only;
+ *                the backward call must see the mask the forward saw.
+ * Work follows the mask: the forward loads and multiplies only the key
+ * tiles that one of a workgroup's two query blocks keeps, the backward only
+ * the (key block, 64-query step) pairs the mask keeps.
+ * bf16 only (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED); N <= 65536 (the
+ * per-workgroup list of visited tiles lives in LDS), else
+ * FA_ERR_UNSUPPORTED.  Other arguments, errors and conventions as for
+ * flash_attn_fwd / flash_attn_bwd; a null block_mask is FA_ERR_INVALID_ARG.
+ */
+#define FA_SPARSE_BLOCK 128
+#define FA_SPARSE_MAX_N 65536
+
+int flash_attn_fwd_blocksparse(const void* q, const void* k, const void* v,
+                               void* o, float* lse, const unsigned char* block_mask,
+                               int B, int H, int N, int d,
+                               float scale, int causal, int dtype, void* stream);
+
+int flash_attn_bwd_blocksparse(const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse,
+                               const unsigned char* block_mask,
+                               void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes,
+                               int B, int H, int N, int d,
+                               float scale, int causal, int dtype, void* stream);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char* flash_attn_status_string(int status);
 

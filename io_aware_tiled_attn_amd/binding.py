@@ -23,6 +23,8 @@ FA_BWD_PREPROCESS = 1
 FA_BWD_MAIN = 2
 FA_BWD_FINALIZE = 4
 FA_BWD_ALL = 7
+FA_SPARSE_BLOCK = 128
+FA_SPARSE_MAX_N = 65536
 
 _lib = None
 
@@ -61,6 +63,10 @@ def _raw():
     lib.flash_attn_bwd.restype = i
     lib.flash_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp, i]
     lib.flash_attn_bwd_ex.restype = i
+    lib.flash_attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_fwd_blocksparse.restype = i
+    lib.flash_attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd_blocksparse.restype = i
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     lib.flash_attn_last_hip_error.argtypes = []
@@ -195,3 +201,81 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, workspace=None
     """Backward pass (all three kernels); see flash_attn_bwd_ex."""
     return flash_attn_bwd_ex(q, k, v, o, lse, do, causal=causal, scale=scale, workspace=workspace,
                              stream=stream, dq=dq, dk=dk, dv=dv, phases=FA_BWD_ALL)
+
+
+def _check_block_mask(block_mask, B, H, N, device):
+    torch = _torch()
+    nb = (N + FA_SPARSE_BLOCK - 1) // FA_SPARSE_BLOCK
+    _check(block_mask, "block_mask", torch.uint8, (B, H, nb, nb))
+    if block_mask.device != device:
+        raise ValueError("block_mask must be on the same device as q")
+
+
+def flash_attn_fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None, lse=None, stream=None):
+    """Block-sparse forward (bfloat16); returns (O, LSE).
+
+    block_mask: uint8 GPU tensor [B, H, nb, nb], nb = ceil(N / 128); entry
+    [b, h, i, j] != 0 keeps (query block i, key block j).  Rows left with no
+    key get O = 0 and LSE = -inf.
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, q.shape)
+    _check_block_mask(block_mask, B, H, N, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.dtype, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           lse.data_ptr(), block_mask.data_ptr(), B, H, N, d, float(scale),
+                                           int(bool(causal)), code, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_blocksparse")
+    return out, lse
+
+
+def flash_attn_bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False, scale=None, workspace=None,
+                               stream=None, dq=None, dk=None, dv=None):
+    """Block-sparse backward (bfloat16); returns (dQ, dK, dV).  o, lse and
+    block_mask as given to / returned by flash_attn_fwd_blocksparse."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (B, H, N))
+    _check_block_mask(block_mask, B, H, N, q.device)
+    need = flash_attn_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check(t, name, q.dtype, q.shape)
+        outs.append(t)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                           lse.data_ptr(), block_mask.data_ptr(), outs[0].data_ptr(),
+                                           outs[1].data_ptr(), outs[2].data_ptr(), workspace.data_ptr(),
+                                           workspace.numel(), B, H, N, d, float(scale), int(bool(causal)), code,
+                                           _stream_ptr(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_blocksparse")
+    return tuple(outs)

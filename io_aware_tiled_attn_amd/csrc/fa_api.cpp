@@ -34,7 +34,8 @@ int check_sizes(int B, int H, int N, int d, float scale, int causal) {
 }
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-             float scale, int causal, int dtype, void* stream, int block_n) {
+             float scale, int causal, int dtype, void* stream, int block_n,
+             const unsigned char* bmask = nullptr) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   int st = check_sizes(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
@@ -44,8 +45,41 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (dtype == FA_DTYPE_BF16 && block_n != 0 && block_n != 32 && block_n != 64)
     return FA_ERR_UNSUPPORTED;
   if (dtype == FA_DTYPE_FP32 && block_n != 0 && block_n != 32) return FA_ERR_UNSUPPORTED;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_n, (hipStream_t)stream};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, dtype, block_n, (hipStream_t)stream, bmask};
   return hip_status(fa::launch_fwd(a));
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+             float scale, int causal, int dtype, void* stream, int phases, const unsigned char* bmask) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  if (phases <= 0 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  const size_t need = flash_attn_bwd_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * N;
+  const size_t acc_padded = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
+  float* dq_acc = static_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_padded);
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dq_acc, delta, B, H, N, d, scale, causal, phases,
+                (hipStream_t)stream, bmask};
+  return hip_status(fa::launch_bwd(a));
+}
+
+// The block-sparse entry points: the dense checks plus the mask pointer,
+// bf16 and the length limit of the LDS tile lists.
+int sparse_checks(const unsigned char* bmask, int N, int d, int dtype) {
+  if (!bmask) return FA_ERR_INVALID_ARG;
+  if (N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (N > FA_SPARSE_MAX_N) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
 }
 
 }  // namespace
@@ -75,24 +109,8 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d) {
 int flash_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
                       int H, int N, int d, float scale, int causal, int dtype, void* stream, int phases) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
-  if (phases <= 0 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_INVALID_ARG;
-  int st = check_sizes(B, H, N, d, scale, causal);
-  if (st != FA_OK) return st;
-  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-  const size_t need = flash_attn_bwd_workspace_size(B, H, N, d);
-  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
-  const size_t rows = (size_t)B * H * N;
-  const size_t acc_padded = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
-  float* dq_acc = static_cast<float*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_padded);
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dq_acc, delta, B, H, N, d, scale, causal, phases,
-                (hipStream_t)stream};
-  return hip_status(fa::launch_bwd(a));
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype,
+                  stream, phases, nullptr);
 }
 
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -100,6 +118,28 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    float scale, int causal, int dtype, void* stream) {
   return flash_attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal,
                            dtype, stream, FA_BWD_ALL);
+}
+
+int flash_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const unsigned char* block_mask, int B, int H, int N, int d, float scale, int causal,
+                               int dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = sparse_checks(block_mask, N, d, dtype);
+  if (st != FA_OK) return st;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, 0, block_mask);
+}
+
+int flash_attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, const unsigned char* block_mask, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                               int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = sparse_checks(block_mask, N, d, dtype);
+  if (st != FA_OK) return st;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype,
+                  stream, FA_BWD_ALL, block_mask);
 }
 
 const char* flash_attn_status_string(int status) {

@@ -113,10 +113,12 @@ __device__ __forceinline__ void bwd_load_stage(BwdStage<D>& st, const BwdHead& h
     st.q[i] = bload128(h.q, off);
     st.g[i] = bload128(h.g, off);
   }
-  // LSE * log2(e) (+inf past N, so P = 0 there) and D (0 past N).
+  // LSE * log2(e) (+inf past N, and for rows that saw no key at all,
+  // LSE = -inf, so P = 0 there) and D (0 past N).
   if (tid < C::BM) {
     const int q = q0 + tid;
-    st.lse2 = q < N ? bload32f(h.lse, (uint32_t)q * 4u) * kLog2e : INFINITY;
+    const float l = q < N ? bload32f(h.lse, (uint32_t)q * 4u) : INFINITY;
+    st.lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
   } else if (tid < 2 * C::BM) {
     st.dlt = bload32f(h.dlt, (uint32_t)(q0 + tid - C::BM) * 4u);
   }
@@ -140,13 +142,18 @@ __device__ __forceinline__ void bwd_store_stage(const BwdStage<D>& st, char* sta
   else if (tid < 2 * C::BM) Ds[tid - C::BM] = st.dlt;
 }
 
-template <int D, bool CAUSAL>
+// SPARSE: block-sparse attention.  bmask holds, per head, an nb x nb byte
+// matrix over (128-query block, 128-key block) pairs (a workgroup's keys are
+// one key block); the workgroup visits only the 64-query steps whose query
+// block its mask column keeps, from a list built in LDS.
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256)
 fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-                   float* __restrict__ dq_acc, __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH,
-                   float scale, float scale_log2) {
+                   float* __restrict__ dq_acc, __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                   const uint8_t* __restrict__ bmask, int N, int BH, float scale, float scale_log2) {
   using C = BwdCfg<D>;
+  static_assert(C::BN == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::BM == 0, "sparse blocks vs tiles");
   constexpr int QB = C::QB;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   __bf16* Kt = (__bf16*)smem_raw;                                  // [D][kKtPitch]
@@ -206,19 +213,41 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     dv_acc[i] = (f32x16){};
   }
 
-  // Query tiles that can see these keys.
+  // Query steps (BM queries each) that can see these keys: qt_begin.. all
+  // of them (dense), or the ones the mask column keeps, listed in LDS after
+  // the other buffers (count first).
   const int qt_begin = CAUSAL ? k0 / C::BM : 0;
-  const int qt_end = (N + C::BM - 1) / C::BM;
+  int n_steps = (N + C::BM - 1) / C::BM - qt_begin;
+  int* slist = (int*)(smem_raw + C::kLdsBytes);
+  if constexpr (SPARSE) {
+    const int nb = (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK;
+    const uint8_t* col = bmask + (size_t)bh * nb * nb + kt;   // entry of query block i at col[i * nb]
+    if (wave == 0) {
+      int cnt = 0;
+      for (int base = 0; base < n_steps; base += 64) {
+        const int qs = qt_begin + base + lane;
+        const bool live = base + lane < n_steps && col[(size_t)(qs * C::BM / FA_SPARSE_BLOCK) * nb] != 0;
+        const uint64_t bal = __ballot(live);
+        const int pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (live) slist[1 + pos] = qs;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) slist[0] = cnt;
+    }
+    __syncthreads();
+    n_steps = __builtin_amdgcn_readfirstlane(slist[0]);
+  }
+  auto step_at = [&](int j) { return SPARSE ? slist[1 + j] : qt_begin + j; };
   BwdStage<D> st;
-  if (qt_begin < qt_end) {
-    bwd_load_stage<D>(st, h, qt_begin * C::BM, N, tid);
+  if (n_steps > 0) {
+    bwd_load_stage<D>(st, h, step_at(0) * C::BM, N, tid);
     bwd_store_stage<D>(st, stages, tid);
   }
 
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
-    const int it = qt - qt_begin;
-    const int q0 = qt * C::BM;
-    if (qt + 1 < qt_end) bwd_load_stage<D>(st, h, q0 + C::BM, N, tid);
+  for (int it = 0; it < n_steps; ++it) {
+    const int q0 = step_at(it) * C::BM;
+    const bool more = it + 1 < n_steps;
+    if (more) bwd_load_stage<D>(st, h, step_at(it + 1) * C::BM, N, tid);
     __syncthreads();   // stage `it` visible; previous dS^T reads finished
     char* stage = stages + (it & 1) * C::kStageBytes;
     const __bf16* Qs = (const __bf16*)stage;
@@ -342,7 +371,7 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
       __builtin_amdgcn_sched_barrier(0);
     }
     update_pairs(1, 0, 2 * DM);
-    if (qt + 1 < qt_end) bwd_store_stage<D>(st, stages + ((it + 1) & 1) * C::kStageBytes, tid);
+    if (more) bwd_store_stage<D>(st, stages + ((it + 1) & 1) * C::kStageBytes, tid);
     __syncthreads();   // dS^T complete
 
     // dQ (BM x D) for this query tile from the workgroup's 128 keys: the
@@ -416,7 +445,7 @@ fa_bwd_dq_finalize_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq
   *(u32x4*)(dq + 8 * i) = w;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   using C = BwdCfg<D>;
   const int BH = a.B * a.H;
@@ -429,12 +458,17 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.phases & FA_BWD_MAIN) {
-    auto kern = fa_bwd_main_kernel<D, CAUSAL>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    auto kern = fa_bwd_main_kernel<D, CAUSAL, SPARSE>;
+    // The sparse kernel keeps its list of visited query steps (count first)
+    // after the other buffers.
+    const int list_bytes = SPARSE ? ((4 * ((a.N + C::BM - 1) / C::BM + 1) + 15) & ~15) : 0;
+    const int lds = C::kLdsBytes + list_bytes;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     const int num_kt = (a.N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL(kern, dim3(num_kt * BH), dim3(C::kThreads), C::kLdsBytes, a.stream, (const __bf16*)a.q,
+    hipLaunchKernelGGL(kern, dim3(num_kt * BH), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta, a.dq_acc,
-                       (__bf16*)a.dk, (__bf16*)a.dv, a.N, BH, a.scale, a.scale * kLog2e);
+                       (__bf16*)a.dk, (__bf16*)a.dv, (const uint8_t*)a.bmask, a.N, BH, a.scale,
+                       a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.phases & FA_BWD_FINALIZE) {
@@ -446,9 +480,14 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   return e;
 }
 
+template <int D, bool SPARSE>
+static hipError_t launch_bwd_c(const BwdArgs& a) {
+  return a.causal ? launch_bwd_d<D, true, SPARSE>(a) : launch_bwd_d<D, false, SPARSE>(a);
+}
+
 hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_bwd_d<64, true>(a) : launch_bwd_d<64, false>(a);
-  return a.causal ? launch_bwd_d<128, true>(a) : launch_bwd_d<128, false>(a);
+  if (a.bmask) return a.d == 64 ? launch_bwd_c<64, true>(a) : launch_bwd_c<128, true>(a);
+  return a.d == 64 ? launch_bwd_c<64, false>(a) : launch_bwd_c<128, false>(a);
 }
 
 }  // namespace fa

@@ -47,6 +47,7 @@
 namespace fa {
 
 constexpr float kPSumLimit = 256.0f;
+constexpr int kSparseBlock = FA_SPARSE_BLOCK;   // block-mask granularity (queries and keys)
 #ifndef FWD_LOOKAHEAD
 #define FWD_LOOKAHEAD 8
 #endif
@@ -194,7 +195,9 @@ __device__ __forceinline__ void softmax_step(const f32x16 (&s)[BN / 32], bf16x8 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
     mx = max_with_lane_xor32(mx) * scale_log2;
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
+    // 0 on the first tile that sees a key; 1 while no key has been seen
+    // (block-sparse rows can start with dropped tiles), where O and l are 0.
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
@@ -252,12 +255,19 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, int BN, bool CAUSAL>
+// SPARSE: block-sparse attention.  bmask holds, per head, an nb x nb byte
+// matrix over (128-query block, 128-key block) pairs; pairs whose byte is 0
+// are masked.  The workgroup (two query blocks) visits only the key tiles
+// that at least one of its query blocks keeps, in order, from a list built
+// in LDS; a wave whose own query block drops a visited tile treats all of
+// that tile's scores as masked.
+template <int D, int BN, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(512)
 fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                   int N, int BH, int num_qt, float scale_log2) {
+                   const uint8_t* __restrict__ bmask, int N, int BH, int num_qt, float scale_log2) {
   using C = FwdCfg<D, BN>;
+  static_assert(C::BM == 2 * kSparseBlock && kSparseBlock % BN == 0, "sparse blocks vs tiles");
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
   const int tid = threadIdx.x;
@@ -317,39 +327,89 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   const int q_tile_end = min(N, (qt + 1) * C::BM);
   const int key_end = CAUSAL ? q_tile_end : N;
-  const int num_kt = (key_end + BN - 1) / BN;
+  int num_kt = (key_end + BN - 1) / BN;
   const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
   auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
-  // Tiles 0 and 1 of each tensor.  Tile t lives in buffer t % 3.
-  copy_tile(0, 0);
-  if (num_kt > 1) copy_tile(1, 1);
+  // Sparse: list of visited key tiles, entry = tile | keep(block 0) << 24 |
+  // keep(block 1) << 25, built by wave 0 with a ballot compaction.
+  int* tlist = (int*)(smem + 2 * C::kBufs * C::kTile);   // [0] = count, then entries
+  if constexpr (SPARSE) {
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const uint8_t* row0 = bmask + ((size_t)bh * nb + 2 * qt) * nb;
+    const bool has1 = 2 * qt + 1 < nb;
+    if (wave == 0) {
+      int cnt = 0;
+      for (int base = 0; base < num_kt; base += 64) {
+        const int t = base + lane;
+        const int kb = t * BN / kSparseBlock;
+        const bool in = t < num_kt;
+        const int k0 = in ? (row0[kb] != 0) : 0;
+        const int k1 = (in && has1) ? (row0[nb + kb] != 0) : 0;
+        const bool live = (k0 | k1) != 0;
+        const uint64_t bal = __ballot(live);
+        const int pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (live) tlist[1 + pos] = t | (k0 << 24) | (k1 << 25);
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) tlist[0] = cnt;
+    }
+    __syncthreads();
+    num_kt = __builtin_amdgcn_readfirstlane(tlist[0]);
+  }
+  auto tile_at = [&](int j) { return SPARSE ? (tlist[1 + j] & 0xFFFFFF) : j; };
+  // Sparse: this wave's query block drops visited tile j.
+  auto dropped = [&](int j) { return SPARSE && !((tlist[1 + j] >> (24 + group)) & 1); };
+
+  // The first two visited tiles of each tensor.  Visited tile j lives in
+  // buffer j % 3.
+  if (num_kt > 0) copy_tile(tile_at(0), 0);
+  if (num_kt > 1) copy_tile(tile_at(1), 1);
   wait_vmem_all();
   __syncthreads();
 
-  // S(0) and P(0).
   f32x16 s[BN / 32];
   bf16x8 pb[BN / 16];
-  score_tile<D, BN>(s, kbuf(0), koff, qb);
-  if (masked(0)) mask_tile<BN>(s, 0, qlim, lg);
-  softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+  // Scores of visited tile j to -inf where masked: all of them when this
+  // wave's query block drops the tile (sparse), else keys past N and, under
+  // the causal mask, keys after the query.
+  auto mask_visit = [&](int j) {
+    const int t = tile_at(j);
+    if (dropped(j)) {
+#pragma unroll
+      for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mb][r] = -INFINITY;
+    } else if (masked(t)) {
+      mask_tile<BN>(s, t * BN, qlim, lg);
+    }
+  };
+
+  // S and P of the first visited tile.
+  if (num_kt > 0) {
+    score_tile<D, BN>(s, kbuf(0), koff, qb);
+    mask_visit(0);
+    softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+  }
 
   // The two waves on each SIMD (waves w and w + 4) alternate: group 1 runs
   // one barrier interval behind group 0, so while one issues the step's
   // MFMAs the other is in its exponentials.  Every wave passes the same
   // number of barriers (group 1 one extra here, group 0 one extra at the
-  // end).  At the start of its matrix phase of step t each group starts the
-  // copy of tile t+2 of its tensor into buffer (t+2) % 3, and waits for it
-  // at the end of its vector phase of the same step.  That buffer's previous
-  // tile (t-1) was last read at least one barrier before the copy starts,
-  // and the new tile is first read at least one barrier after the wait.
+  // end).  Step t works on visited tiles t and t+1 (all key tiles in
+  // order, dense).  At the start of its matrix phase of step t each group
+  // starts the copy of visited tile t+2 of its tensor into buffer (t+2) % 3,
+  // and waits for it at the end of its vector phase of the same step.  That
+  // buffer's previous tile (t-1) was last read at least one barrier before
+  // the copy starts, and the new tile is first read at least one barrier
+  // after the wait.
   if (group == 1) __syncthreads();
 
   int b_cur = 0;   // t % 3
   for (int t = 0; t < num_kt; ++t) {
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;    // (t + 1) % 3
     const int b_copy = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
-    if (t + 2 < num_kt) copy_tile(t + 2, b_copy);
+    if (t + 2 < num_kt) copy_tile(tile_at(t + 2), b_copy);
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
     // wave runs the same instruction stream on every step: on causal tiles
     // wholly above a wave's queries its P is all zero (the tile is masked
@@ -359,7 +419,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1).
     if (t + 1 < num_kt) {
-      if (masked(t + 1)) mask_tile<BN>(s, (t + 1) * BN, qlim, lg);
+      mask_visit(t + 1);
       softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     }
     wait_vmem_all();
@@ -470,17 +530,21 @@ fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bf16(const FwdArgs& a) {
   using C = FwdCfg<D, BN>;
   const int BH = a.B * a.H;
   const int num_qt = (a.N + C::BM - 1) / C::BM;
-  auto kern = fa_fwd_bf16_kernel<D, BN, CAUSAL>;
+  auto kern = fa_fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>;
+  // The sparse kernel keeps its list of visited key tiles (count first)
+  // after the tile buffers.
+  const int list_bytes = SPARSE ? ((4 * ((a.N + BN - 1) / BN + 1) + 15) & ~15) : 0;
+  const int lds = C::kLdsBytes + list_bytes;
   // Dynamic LDS above 64 KB must be allowed explicitly; setting the same
   // value from several threads is harmless.
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-  hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), C::kLdsBytes, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.N, BH,
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q,
+                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, (const uint8_t*)a.bmask, a.N, BH,
                      num_qt, a.scale * kLog2e);
   return hipGetLastError();
 }
@@ -498,7 +562,8 @@ static hipError_t launch_f32(const FwdArgs& a) {
 
 template <int D, int BN>
 static hipError_t launch_bf16_bn(const FwdArgs& a) {
-  return a.causal ? launch_bf16<D, BN, true>(a) : launch_bf16<D, BN, false>(a);
+  if (a.bmask) return a.causal ? launch_bf16<D, BN, true, true>(a) : launch_bf16<D, BN, false, true>(a);
+  return a.causal ? launch_bf16<D, BN, true, false>(a) : launch_bf16<D, BN, false, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {

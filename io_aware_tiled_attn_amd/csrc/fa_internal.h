@@ -21,6 +21,7 @@ struct FwdArgs {
   int dtype;
   int block_n;   // 0 = default
   hipStream_t stream;
+  const unsigned char* bmask;   // block-sparse mask [B, H, nb, nb], or null (dense)
 };
 
 struct BwdArgs {
@@ -40,6 +41,7 @@ struct BwdArgs {
   int causal;
   int phases;     // FA_BWD_* mask
   hipStream_t stream;
+  const unsigned char* bmask;   // block-sparse mask [B, H, nb, nb], or null (dense)
 };
 
 hipError_t launch_fwd(const FwdArgs& a);

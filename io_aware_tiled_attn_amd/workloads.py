@@ -107,3 +107,36 @@ def workload_inputs(name, with_grad=None):
     if with_grad is None:
         with_grad = w.backward
     return make_inputs(w.shape, w.seed, w.dtype, with_grad)
+
+
+# ---------------------------------------------------------------------------
+# Block masks for block-sparse attention: one byte per (128-query block,
+# 128-key block) pair, [B, H, nb, nb] with nb = ceil(N / 128); nonzero keeps
+# the pair.  Structure only, no attention arithmetic.
+# ---------------------------------------------------------------------------
+SPARSE_BLOCK = 128
+
+
+def random_block_mask(B, H, N, seed, density=0.5, block=SPARSE_BLOCK):
+    """Each pair kept independently with probability `density` (PCG64)."""
+    nb = -(-N // block)
+    rng = np.random.default_rng(seed)
+    return (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
+
+
+def local_global_block_mask(B, H, N, band=2, block=SPARSE_BLOCK):
+    """A local band of blocks (|i - j| <= band) plus the first key block
+    (a global column), the same for every head."""
+    nb = -(-N // block)
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    m = ((np.abs(i - j) <= band) | (j == 0)).astype(np.uint8)
+    return np.ascontiguousarray(np.broadcast_to(m, (B, H, nb, nb)))
+
+
+# Block-sparse workload the benchmark reports beside the dense one: the
+# N=4096, d=128 shape with the local+global mask (6 of 32 key blocks per
+# query block at most, about 17 % of the pairs), non-causal, forward and
+# backward.
+SPARSE_WORKLOAD = Workload("bf16_n4k_d128_blocksparse", 4, 32, 4096, 128, "bf16", False, True, 6,
+                           "block-sparse (local band 2 + global first block), forward+backward")

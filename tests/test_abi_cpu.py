@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["flash_attn_fwd", "flash_attn_fwd_ex", "flash_attn_bwd", "flash_attn_bwd_ex",
                             "flash_attn_bwd_workspace_size", "flash_attn_status_string",
-                            "flash_attn_last_hip_error"])
+                            "flash_attn_last_hip_error", "flash_attn_fwd_blocksparse",
+                            "flash_attn_bwd_blocksparse"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -132,3 +133,50 @@ def test_python_binding_requires_gpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding.flash_attn_fwd(q, q, q)
+
+
+def fwd_sparse(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, mask=FAKE, B=1, H=1, N=16, d=64, scale=0.125, causal=0,
+             dtype=binding.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["B"],
+                                                     a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                                     a["stream"])
+
+
+def bwd_sparse(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, mask=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 40, B=1, H=1, N=16, d=64, scale=0.125, causal=1,
+             dtype=binding.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_bwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["mask"],
+                                                     a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"], a["B"],
+                                                     a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), binding.FA_ERR_INVALID_ARG),
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), binding.FA_ERR_INVALID_ARG),
+    (dict(N=binding.FA_SPARSE_MAX_N + 1), binding.FA_ERR_UNSUPPORTED),
+    (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), binding.FA_ERR_INVALID_ARG),
+    (dict(o=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+])
+def test_sparse_forward_rejects_bad_arguments(kw, code):
+    assert fwd_sparse(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ws=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), binding.FA_ERR_INVALID_ARG),
+    (dict(N=binding.FA_SPARSE_MAX_N + 1), binding.FA_ERR_UNSUPPORTED),
+    (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+    (dict(dk=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+])
+def test_sparse_backward_rejects_bad_arguments(kw, code):
+    assert bwd_sparse(**kw) == code
