@@ -312,8 +312,11 @@ def main():
     }
     if not args.no_blocksparse:
         print("[bench] block-sparse step", file=sys.stderr, flush=True)
-        result["blocksparse"] = blocksparse_step(q, k, v, do, o, lse, dq, dk, dv, ws, stream, ms_per_step,
-                                                 max(5, args.warmup // 2), max(10, args.steps // 2))
+        # Separate outputs: the dense step's results are still checked below.
+        result["blocksparse"] = blocksparse_step(q, k, v, do, torch.empty_like(o), torch.empty_like(lse),
+                                                 torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv),
+                                                 ws, stream, ms_per_step, max(5, args.warmup // 2),
+                                                 max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         gpu_out = {"o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.float().cpu().numpy(),
