@@ -22,6 +22,7 @@ from .attention import (  # noqa: F401
     attention_forward_head,
     attention_backward,
     attention_backward_head,
+    attention_decode_head,
     safe_softmax,
     default_scale,
 )

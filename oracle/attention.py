@@ -33,6 +33,12 @@ Readings where the pages are silent:
     the scores of every pair whose mask entry is 0 are -inf (weight 0), the
     rest is ordinary attention.  Rows left with no key get O = 0, LSE = -inf
     and zero gradients.
+  * decoding with a key/value cache: the pages only ask which parts of the
+    speed-up carry over to autoregressive decoding with a KV cache
+    (chorfi.xyz, "Discussion prompts").  Reading: Nq new queries attend to
+    an Nk-entry cache (Nq <= Nk); they are the cache's last Nq positions, so
+    under the causal mask query i sees keys j <= Nk - Nq + i (the same rule
+    as above, shifted by Nk - Nq); without it every query sees every key.
   * backward: the pages only say the backward pass recomputes attention
     instead of storing it (chorfi.xyz "Study objectives"; modelfieldguide.com
     "An IO-aware rewrite").  The gradients below are the calculus of the
@@ -76,10 +82,10 @@ def safe_softmax(s):
     return e / l, float(m), l
 
 
-def _causal_mask(row_idx, n_keys):
-    """True where key j > query i (masked)."""
+def _causal_mask(row_idx, n_keys, offset=0):
+    """True where key j > query i + offset (masked)."""
     j = np.arange(n_keys)[None, :]
-    return j > np.asarray(row_idx)[:, None]
+    return j > np.asarray(row_idx)[:, None] + offset
 
 
 def _block_masked(row_idx, n_keys, block_mask, block):
@@ -92,13 +98,15 @@ def _block_masked(row_idx, n_keys, block_mask, block):
     return ~bm[qb][:, kb]
 
 
-def attention_forward_head(q, k, v, scale=None, causal=False, rows=None, block_mask=None, block=(128, 128)):
+def attention_forward_head(q, k, v, scale=None, causal=False, rows=None, block_mask=None, block=(128, 128),
+                           causal_offset=0):
     """Exact attention for one head.
 
     q: [Nq, d], k: [Nk, d], v: [Nk, dv], any real dtype (promoted to float64).
     rows: optional index array of query rows to evaluate (default: all).
     block_mask: optional [ceil(Nq/bq), ceil(Nk/bk)] array for block-sparse
     attention, block = (bq, bk); pairs whose entry is 0 are masked.
+    causal_offset: under the causal mask, query i sees keys j <= i + offset.
     Returns (O [len(rows), dv], LSE [len(rows)]) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -116,7 +124,7 @@ def attention_forward_head(q, k, v, scale=None, causal=False, rows=None, block_m
         r = rows[c0:c0 + _ROW_CHUNK]
         s = scale * (q[r] @ k.T)                       # scores, [rows, Nk]
         if causal:
-            s[_causal_mask(r, n_keys)] = -np.inf
+            s[_causal_mask(r, n_keys, causal_offset)] = -np.inf
         if block_mask is not None:
             s[_block_masked(r, n_keys, block_mask, block)] = -np.inf
         m = np.max(s, axis=1)                          # row max
@@ -196,3 +204,11 @@ def attention_backward(q, k, v, do, scale=None, causal=False, block_mask=None, b
                 q[b, h], k[b, h], v[b, h], do[b, h], scale=scale, causal=causal,
                 block_mask=None if block_mask is None else block_mask[b, h], block=block)
     return dq, dk, dv
+
+
+def attention_decode_head(q, k, v, scale=None, causal=False):
+    """Nq new queries (the cache's last Nq positions) against an Nk-entry
+    key/value cache: q [Nq, d], k [Nk, d], v [Nk, dv], Nq <= Nk.  Causal:
+    query i sees keys j <= Nk - Nq + i.  Returns (O [Nq, dv], LSE [Nq])."""
+    n_q, n_k = np.asarray(q).shape[0], np.asarray(k).shape[0]
+    return attention_forward_head(q, k, v, scale=scale, causal=causal, causal_offset=n_k - n_q)

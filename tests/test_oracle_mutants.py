@@ -41,6 +41,8 @@ MUTANTS = {
                          "        pass"),
     "block_mask_transposed": ("    return ~bm[qb][:, kb]", "    return ~bm.T[qb][:, kb]"),
     "block_rows_use_key_block_size": ("    qb = np.asarray(row_idx) // bq", "    qb = np.asarray(row_idx) // bk"),
+    "decode_offset_dropped": ("causal=causal, causal_offset=n_k - n_q)", "causal=causal, causal_offset=0)"),
+    "decode_offset_sign": ("causal=causal, causal_offset=n_k - n_q)", "causal=causal, causal_offset=n_q - n_k)"),
     "bwd_block_mask_dropped": ("        s[_block_masked(np.arange(n_q), n_k, block_mask, block)] = -np.inf",
                                "        pass"),
 }
@@ -145,6 +147,14 @@ def _battery(mod):
             failed.append("block_autograd")
     except Exception:
         failed.append("block_raised")
+    # Decoding: the last queries against the whole cache equal the last rows
+    # of the full causal attention (scalar loops).
+    nq, nk = 3, 8
+    q, k, v = (rng.standard_normal((nk, 3)) for _ in range(3))
+    o, lse = mod.attention_decode_head(q[nk - nq:], k, v, scale=0.6, causal=True)
+    bo, bl = _brute(q.tolist(), k.tolist(), v.tolist(), 0.6, True)
+    if not (np.allclose(o, bo[nk - nq:], atol=1e-12) and np.allclose(lse, bl[nk - nq:], atol=1e-12)):
+        failed.append("decode_brute")
     return failed
 
 
