@@ -30,7 +30,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published figure
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["io_aware_tiled_attn_amd/csrc/fa_fwd.hip", "io_aware_tiled_attn_amd/csrc/fa_bwd.hip",
-                  "io_aware_tiled_attn_amd/csrc/fa_common.h"]
+                  "io_aware_tiled_attn_amd/csrc/fa_decode.hip", "io_aware_tiled_attn_amd/csrc/fa_common.h"]
 
 
 def parse_args():
@@ -42,6 +42,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the KV-cache decoding step reported beside the dense one")
     ap.add_argument("--no-blocksparse", action="store_true",
                     help="skip the block-sparse step reported beside the dense one")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -187,6 +189,47 @@ def blocksparse_step(q, k, v, do, o, lse, dq, dk, dv, ws, stream, dense_ms, warm
     }
 
 
+def decode_step(warmup, steps):
+    """Decoding against a KV cache (split-KV): one new query per head of a
+    B=16, H=32, 8192-entry d=128 cache, the inputs drawn with the workload's
+    recipe.  HBM-bound: the roofline is bytes moved (Q, K, V read, O and LSE
+    written, the split partials counted too) over the 8 TB/s HBM peak."""
+    import numpy as np
+    import torch
+    import io_aware_tiled_attn_amd as fa
+    from io_aware_tiled_attn_amd import workloads as wl
+    w = wl.DECODE_WORKLOAD
+    inp = wl.decode_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.seed)
+    q, k, v = (torch.from_numpy(inp[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.flash_attn_decode_workspace_size(w.B, w.H, w.Nk, w.d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.flash_attn_decode(q, k, v, causal=w.causal, out=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fa.flash_attn_decode(q, k, v, causal=w.causal, out=o, lse=lse, workspace=ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kv_bytes = 2.0 * w.B * w.H * w.Nk * w.d * 2
+    qo_bytes = 2.0 * w.B * w.H * w.Nq * w.d * 2 + 4.0 * w.B * w.H * w.Nq
+    part_bytes = 2.0 * ws.numel()   # split partials written, then read by the merge
+    gbs = (kv_bytes + qo_bytes + part_bytes) / (ms * 1e-3) / 1e9
+    return {
+        "workload": "%s: B=%d H=%d Nq=%d Nk=%d d=%d bf16, %s" % (w.name, w.B, w.H, w.Nq, w.Nk, w.d,
+                                                               "causal" if w.causal else "non-causal"),
+        "ms": round(ms, 4),
+        "tokens_per_s": round(w.B * w.Nq / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": int(kv_bytes + qo_bytes + part_bytes)},
+    }
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -317,6 +360,9 @@ def main():
                                                  torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv),
                                                  ws, stream, ms_per_step, max(5, args.warmup // 2),
                                                  max(10, args.steps // 2))
+    if not args.no_decode:
+        print("[bench] decoding step", file=sys.stderr, flush=True)
+        result["decode"] = decode_step(max(5, args.warmup // 2), args.steps)
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         gpu_out = {"o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.float().cpu().numpy(),

@@ -201,6 +201,33 @@ int flash_attn_bwd_blocksparse(const void* q, const void* k, const void* v,
                                int B, int H, int N, int d,
                                float scale, int causal, int dtype, void* stream);
 
+/*
+ * Decoding with a key/value cache (split-KV).  The pages ask which parts of
+ * the speed-up carry over to autoregressive decoding with a KV cache
+ * (chorfi.xyz study guide, "Discussion prompts").  Here: Nq new queries per
+ * head (1 <= Nq <= FA_DECODE_MAX_Q) attend to an Nk-entry cache
+ * (Nq <= Nk); they are the cache's last Nq positions, so with causal = 1
+ * query i sees keys j <= Nk - Nq + i, and with causal = 0 every key.  The
+ * keys are split across waves; each split runs the online-softmax rule of
+ * the forward pass and the splits are merged with the same rule.
+ *   q        : [B, H, Nq, d] bf16.   k, v : [B, H, Nk, d] bf16 (the cache).
+ *   o        : [B, H, Nq, d] bf16, written.   lse : [B, H, Nq] fp32 or NULL.
+ *   workspace: at least flash_attn_decode_workspace_size(B, H, Nk, d) bytes,
+ *              256-byte aligned (per-split partial results), clobbered.
+ * bf16 only; d in {64, 128}; B*H*Nk*d below 2^31.  Errors as for
+ * flash_attn_fwd, plus FA_ERR_UNSUPPORTED for Nq > FA_DECODE_MAX_Q and
+ * FA_ERR_INVALID_ARG for Nq > Nk or a null or short workspace.
+ */
+#define FA_DECODE_MAX_Q 16
+
+size_t flash_attn_decode_workspace_size(int B, int H, int Nk, int d);
+
+int flash_attn_decode(const void* q, const void* k, const void* v,
+                      void* o, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int Nq, int Nk, int d,
+                      float scale, int causal, int dtype, void* stream);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char* flash_attn_status_string(int status);
 

@@ -14,6 +14,8 @@ __all__ = [
     "flash_attn_bwd_ex",
     "flash_attn_fwd_blocksparse",
     "flash_attn_bwd_blocksparse",
+    "flash_attn_decode",
+    "flash_attn_decode_workspace_size",
     "flash_attn_bwd_workspace_size",
     "flash_attn_status_string",
     "FlashAttnError",

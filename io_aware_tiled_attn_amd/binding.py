@@ -25,6 +25,7 @@ FA_BWD_FINALIZE = 4
 FA_BWD_ALL = 7
 FA_SPARSE_BLOCK = 128
 FA_SPARSE_MAX_N = 65536
+FA_DECODE_MAX_Q = 16
 
 _lib = None
 
@@ -67,6 +68,10 @@ def _raw():
     lib.flash_attn_fwd_blocksparse.restype = i
     lib.flash_attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
     lib.flash_attn_bwd_blocksparse.restype = i
+    lib.flash_attn_decode_workspace_size.argtypes = [i, i, i, i]
+    lib.flash_attn_decode_workspace_size.restype = sz
+    lib.flash_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_decode.restype = i
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     lib.flash_attn_last_hip_error.argtypes = []
@@ -279,3 +284,47 @@ def flash_attn_bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False, sc
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_blocksparse")
     return tuple(outs)
+
+
+def flash_attn_decode_workspace_size(B, H, Nk, d):
+    return int(_raw().flash_attn_decode_workspace_size(int(B), int(H), int(Nk), int(d)))
+
+
+def flash_attn_decode(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Decoding against a key/value cache (bfloat16); returns (O, LSE).
+
+    q: [B, H, Nq, d] with 1 <= Nq <= 16; k, v: [B, H, Nk, d], Nk >= Nq.
+    The queries are the cache's last Nq positions (causal: query i sees keys
+    j <= Nk - Nq + i).  workspace, if given, is a uint8 GPU tensor of at
+    least flash_attn_decode_workspace_size(B, H, Nk, d) bytes.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    code = _dtype_code(q)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, H, Nk, d))
+    _check(v, "v", q.dtype, (B, H, Nk, d))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.dtype, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, Nq))
+    need = flash_attn_decode_workspace_size(B, H, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel(), B, H, Nq, Nk, d, float(scale),
+                                  int(bool(causal)), code, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_decode")
+    return out, lse

@@ -142,6 +142,36 @@ int flash_attn_bwd_blocksparse(const void* q, const void* k, const void* v, cons
                   stream, FA_BWD_ALL, block_mask);
 }
 
+size_t flash_attn_decode_workspace_size(int B, int H, int Nk, int d) {
+  if (B < 1 || H < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+  if ((long long)B * H * Nk * d > kMaxElems) return 0;
+  return fa::decode_workspace_bytes(B, H, Nk, d);
+}
+
+int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      void* stream) {
+  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * Nk * d > kMaxElems) return FA_ERR_INVALID_ARG;
+  if (Nq > Nk) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Nq > FA_DECODE_MAX_Q) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_INVALID_ARG;
+  const size_t need = fa::decode_workspace_bytes(B, H, Nk, d);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  // Layout: partial O (256-byte aligned), then partial LSE.
+  float* part_o = static_cast<float*>(workspace);
+  fa::DecodeArgs a{q, k, v, o, lse, part_o, nullptr, B, H, Nq, Nk, d, scale, causal, (hipStream_t)stream};
+  a.part_lse = fa::decode_part_lse(part_o, B, H, Nk, d);
+  return hip_status(fa::launch_decode(a));
+}
+
 const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

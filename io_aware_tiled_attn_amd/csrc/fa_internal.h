@@ -44,7 +44,24 @@ struct BwdArgs {
   const unsigned char* bmask;   // block-sparse mask [B, H, nb, nb], or null (dense)
 };
 
+struct DecodeArgs {
+  const void* q;   // [B, H, Nq, d]
+  const void* k;   // [B, H, Nk, d]
+  const void* v;
+  void* o;         // [B, H, Nq, d]
+  float* lse;      // [B, H, Nq] or null
+  float* part_o;   // workspace: fp32 [B*H*splits, 16, d]
+  float* part_lse; // workspace: fp32 [B*H*splits, 16]
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+size_t decode_workspace_bytes(int B, int H, int Nk, int d);   // valid sizes only
+float* decode_part_lse(float* part_o, int B, int H, int Nk, int d);   // LSE part of the workspace
 
 }  // namespace fa

@@ -140,3 +140,30 @@ def local_global_block_mask(B, H, N, band=2, block=SPARSE_BLOCK):
 # backward.
 SPARSE_WORKLOAD = Workload("bf16_n4k_d128_blocksparse", 4, 32, 4096, 128, "bf16", False, True, 6,
                            "block-sparse (local band 2 + global first block), forward+backward")
+
+
+# Decoding against a key/value cache: Nq new queries per head and an
+# Nk-entry cache.  Recipe: rng = default_rng(seed); Q [B,H,Nq,d], then K and
+# V [B,H,Nk,d], standard normal float32, rounded to bf16.
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+
+
+DECODE_WORKLOAD = DecodeWorkload("bf16_decode_b16_h32_q1_nk8k_d128", 16, 32, 1, 8192, 128, False, 7)
+
+
+def decode_inputs(B, H, Nq, Nk, d, seed):
+    """bf16 bit patterns (uint16) of Q, K, V for a decoding call."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["flash_attn_fwd", "flash_attn_fwd_ex", "flash_attn_bwd", "flash_attn_bwd_ex",
                             "flash_attn_bwd_workspace_size", "flash_attn_status_string",
                             "flash_attn_last_hip_error", "flash_attn_fwd_blocksparse",
-                            "flash_attn_bwd_blocksparse"])
+                            "flash_attn_bwd_blocksparse", "flash_attn_decode",
+                            "flash_attn_decode_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -180,3 +181,37 @@ def test_sparse_forward_rejects_bad_arguments(kw, code):
 ])
 def test_sparse_backward_rejects_bad_arguments(kw, code):
     assert bwd_sparse(**kw) == code
+
+
+def decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 40, B=1, H=1,
+             Nq=1, Nk=64, d=128, scale=0.125, causal=0, dtype=binding.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["ws_bytes"],
+                                            a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                            a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ws=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), binding.FA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x10010)), binding.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), binding.FA_ERR_INVALID_ARG),
+    (dict(Nq=65), binding.FA_ERR_INVALID_ARG),           # more queries than cache entries
+    (dict(Nq=17, Nk=100), binding.FA_ERR_UNSUPPORTED),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+    (dict(causal=3), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(k=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_workspace_size():
+    f = binding.flash_attn_decode_workspace_size
+    assert f(16, 32, 8192, 128) > 0 and f(16, 32, 8192, 128) % 256 == 0
+    assert f(1, 1, 1, 64) > 0
+    assert f(0, 1, 64, 64) == 0 and f(1, 1, 64, 96) == 0
