@@ -167,3 +167,39 @@ def decode_inputs(B, H, Nq, Nk, d, seed):
     k = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
     v = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
     return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
+
+
+# ---------------------------------------------------------------------------
+# FP8 inputs.  Recipe: the same seeded N(0, 1) float32 draws as a workload
+# (Q, K, V in that order); each tensor gets one descale factor
+# s = max|x| / 448 (rounded to float32) and is stored as the E4M3 codes of
+# x / s, rounded to nearest even by torch's float8_e4m3fn conversion (values
+# clipped to +-448 first).  The stored tensor stands for codes * s.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x):
+    """(uint8 E4M3 codes, float32 descale) of a float32 array, per tensor."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    y = np.clip(x / np.float32(descale), -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, descale
+
+
+def fp8_inputs(shape, seed):
+    """E4M3 codes and descale factors of Q, K, V:
+    {"q": codes, "q_descale": s, "k": ..., "k_descale": ..., "v": ..., "v_descale": ...}."""
+    out = {}
+    for name, a in zip(("q", "k", "v"), draw(tuple(shape), seed, 3)):
+        out[name], out[name + "_descale"] = quantize_e4m3(a)
+    return out
+
+
+# FP8 forward reported beside the bf16 step: the N=4096, d=128 causal shape,
+# quantized from the same draws (seed 3) as the bf16 workload.
+FP8_WORKLOAD = Workload("fp8_n4k_d128_causal", 4, 32, 4096, 128, "fp8", True, False, 3,
+                        "FP8 (E4M3, per-tensor descale) B4 H32 N4096 d128, causal, forward")

@@ -12,6 +12,7 @@ values.  The backward pass is the analytic gradient of that definition.
 
 Module map:
   attention  - forward (O and per-row log-sum-exp) and backward (dQ, dK, dV).
+  fp8        - E4M3 decoding and attention of dequantized FP8 inputs.
   online     - the pages' block-by-block update rule (running max, running sum,
                rescaled output accumulator) in float64.  Tests use it only to
                check the pages' own assertions; it is not the parity target.
@@ -25,5 +26,11 @@ from .attention import (  # noqa: F401
     attention_decode_head,
     safe_softmax,
     default_scale,
+)
+from .fp8 import (  # noqa: F401
+    e4m3_to_float64,
+    dequantize,
+    attention_forward_fp8_head,
+    attention_weights_fp8_head,
 )
 from .online import online_softmax, tiled_attention  # noqa: F401
