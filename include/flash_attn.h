@@ -228,6 +228,31 @@ int flash_attn_decode(const void* q, const void* k, const void* v,
                       int B, int H, int Nq, int Nk, int d,
                       float scale, int causal, int dtype, void* stream);
 
+/*
+ * FP8 forward.  The pages list FP8 support as part of FlashAttention-3's
+ * rebuild for newer hardware (vibeengines.com, "FlashAttention, explained",
+ * section "Why it still matters") without defining it.  Here: Q, K and V are
+ * stored as 8-bit E4M3 codes (OCP 8-bit floating point, E4M3 variant: sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, codes 0x7F
+ * and 0xFF are NaN, largest finite value 448), one byte per element in the
+ * [B, H, N, d] layout, each tensor with one float descale factor: the value
+ * of a Q element is e4m3(code) * q_descale, likewise for K and V.  The
+ * result is the attention defined above of those values, O in bf16 and LSE
+ * in fp32.  Both products run on the FP8 matrix cores; the probabilities
+ * enter the second product rounded to E4M3, so O carries that rounding (a
+ * relative error of up to 2^-4 per probability); LSE does not.
+ *   q, k, v      : [B, H, N, d] E4M3 codes, read only.
+ *   *_descale    : finite and > 0.
+ *   o            : [B, H, N, d] bf16, written.   lse : [B, H, N] fp32 or NULL.
+ * Errors as for flash_attn_fwd (a descale that is not finite and > 0 is
+ * FA_ERR_INVALID_ARG); d in {64, 128}.
+ */
+int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
+                       float q_descale, float k_descale, float v_descale,
+                       void* o, float* lse,
+                       int B, int H, int N, int d,
+                       float scale, int causal, void* stream);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char* flash_attn_status_string(int status);
 

@@ -10,6 +10,7 @@ the first call does, and it raises if the library has not been built.
 __all__ = [
     "flash_attn_fwd",
     "flash_attn_fwd_ex",
+    "flash_attn_fwd_fp8",
     "flash_attn_bwd",
     "flash_attn_bwd_ex",
     "flash_attn_fwd_blocksparse",

@@ -72,6 +72,8 @@ def _raw():
     lib.flash_attn_decode_workspace_size.restype = sz
     lib.flash_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.flash_attn_decode.restype = i
+    lib.flash_attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, f, i, vp]
+    lib.flash_attn_fwd_fp8.restype = i
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     lib.flash_attn_last_hip_error.argtypes = []
@@ -157,6 +159,40 @@ def flash_attn_fwd_ex(q, k, v, causal=False, scale=None, block_n=0, out=None, ls
 def flash_attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     """Forward pass; see flash_attn_fwd_ex."""
     return flash_attn_fwd_ex(q, k, v, causal=causal, scale=scale, block_n=0, out=out, lse=lse, stream=stream)
+
+
+def flash_attn_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, out=None, lse=None,
+                       stream=None):
+    """FP8 forward on [B, H, N, d] E4M3 codes; returns (O bf16, LSE fp32).
+
+    q, k, v: contiguous GPU tensors of dtype uint8 (the codes) or
+    float8_e4m3fn, same shape; the *_descale floats give each tensor's
+    values as code value * descale.  scale defaults to 1/sqrt(d).
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError(f"q has dtype {q.dtype}, expected uint8 or float8_e4m3fn")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, q.shape)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check(out, "out", torch.bfloat16, (B, H, N, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_descale), float(k_descale),
+                                   float(v_descale), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                                   int(bool(causal)), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_fp8")
+    return out, lse
 
 
 def flash_attn_bwd_ex(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, stream=None,

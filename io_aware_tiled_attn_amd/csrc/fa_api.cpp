@@ -96,6 +96,22 @@ int flash_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, floa
   return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, block_n);
 }
 
+int flash_attn_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
+                       float v_descale, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                       void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  const float ds[] = {q_descale, k_descale, v_descale};
+  for (float x : ds)
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_INVALID_ARG;
+  fa::FwdFp8Args a{q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, N, d, scale, causal,
+                   (hipStream_t)stream};
+  return hip_status(fa::launch_fwd_fp8(a));
+}
+
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   if ((long long)B * H * N * d > kMaxElems) return 0;

@@ -109,6 +109,21 @@ __device__ __forceinline__ void batomic_add(__amdgpu_buffer_rsrc_t r, uint32_t o
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)off, 0, 0);
 }
 
+// One buffer_load_dwordx4 ... lds: each lane's 16 bytes at byte offset goff
+// of the buffer go to LDS address lds_addr + 16 * lane (lds_addr is uniform
+// and travels in M0).  Written as inline assembly so that the compiler does
+// not guard every later LDS read of this wave with a wait for the copy (it
+// cannot tell which LDS bytes the copy writes); the kernel orders the copy
+// itself, with an explicit vmcnt wait and a barrier before any read of the
+// bytes it fills.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t goff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(goff), "s"(r), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(0), leaving the other counters alone.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Work order for a launch of num_tiles x BH workgroups (tile-major work
 // items of BH heads).  The dispatcher hands workgroup i to XCD i % 8, and
 // each XCD has its own L2.  When BH is a multiple of 8, XCD x takes heads

@@ -85,18 +85,6 @@ struct Swizzle {
   __device__ static int v(int r) { return 4 * ((r / kRpb) % (kCpr / 4)); }
 };
 
-// One buffer_load_dwordx4 ... lds: each lane's 16 bytes at byte offset goff
-// of the buffer go to LDS address lds_addr + 16 * lane (lds_addr is uniform
-// and travels in M0).  Written as inline assembly so that the compiler does
-// not guard every later LDS read of this wave with a wait for the copy (it
-// cannot tell which LDS bytes the copy writes); the kernel orders the copy
-// itself, with an explicit vmcnt wait and a barrier before any read of the
-// bytes it fills.
-__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t goff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(goff), "s"(r), "{m0}"(lds_addr)
-               : "memory");
-}
-
 // Global -> LDS without registers (buffer_load ... lds): this wave's share
 // of a BN x D tile starting at key j0.  Each instruction fills 1 KB of LDS
 // in lane order (lane i writes bytes 16i..16i+15); lane i therefore loads
@@ -117,9 +105,6 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile,
     lds_copy16(r, goff, (uint32_t)(uintptr_t)(tile + inst * 512));
   }
 }
-
-// s_waitcnt vmcnt(0), leaving the other counters alone.
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // S^T = K Q^T for one tile: BN keys x this wave's 32 queries.  The k-steps
 // run outermost so the BN/32 accumulator chains interleave.

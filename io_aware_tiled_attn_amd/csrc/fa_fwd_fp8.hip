@@ -1,0 +1,370 @@
+// FP8 forward attention kernel for gfx950.
+//
+// Same method as the bf16 forward (exact attention by key tiles with the
+// online-softmax update: vibeengines.com "FlashAttention, explained",
+// sections "Tiling and the online softmax" and "The math, worked with real
+// numbers"), with Q, K and V stored as E4M3 codes and one descale factor per
+// tensor (FP8 support is the FlashAttention-3 step of the lineage table in
+// that page's section "Why it still matters").  Both products run on
+// v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32), twice the bf16 rate:
+//   * S^T = K Q^T: the descales and the softmax scale fold into the single
+//     factor applied before exp2, so the codes enter the product unchanged.
+//   * O^T += V^T P^T: P = exp2(s - m) in fp32, rounded to E4M3 (round to
+//     nearest even).  The lazy reference m keeps every P <= 256, inside
+//     E4M3's range (448); the running sum l is taken from the fp32 P.  O is
+//     scaled by v_descale / l at the end.
+//
+// Layout (one workgroup = 8 waves = 256 query rows, 64-key tiles):
+//   * each wave owns 32 queries; its Q slice (codes) lives in registers as
+//     the B operand of S^T = K Q^T, one query per lane column.
+//   * K and V tiles are copied into LDS straight from global memory
+//     (buffer_load ... lds), three buffers each; waves 0-3 copy K, waves 4-7
+//     V.  The matrix/vector ping-pong of the two wave groups is the bf16
+//     kernel's.
+//   * The 32x32x64 product's k-dimension is any order both operands agree
+//     on.  S^T's row rho of each 32-key block is key kperm(rho) (bits
+//     [a1 a0 h b1 b0] of rho -> [h a1 a0 b1 b0]), so register r of lane half
+//     h holds key 16 h + r, and the P values of a lane half, in register
+//     order, are the 64-key tile's keys {32 b + 16 h + 0..15 : b = 0, 1}.
+//     V^T's matching A operand is four ds_read_b64_tr_b8 reads (8
+//     consecutive keys of one feature column each).
+//   * Rows in LDS are unpadded with their 16-byte chunks XOR-permuted so the
+//     K reads (16 lanes, rows {0..7, 16..23} or {8..15, 24..31} of a block, one
+//     chunk) and the V transposing reads (32 lanes, 8 consecutive rows, two
+//     adjacent chunks) hit distinct banks.
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr float kFp8PSumLimit = 256.0f;   // bound on every P; E4M3 holds up to 448
+
+// v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 and no block scales.
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D>
+struct Fp8Cfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int BM = kWaves * 32;
+  static constexpr int BN = 64;            // keys per tile: the k of one P V product
+  static constexpr int kTile = BN * D;     // bytes of one K or V tile
+  static constexpr int kBufs = 3;
+  static constexpr int kLdsBytes = 2 * kBufs * kTile;
+  static constexpr int kDmaPerWave = kTile / 1024 / 4;   // 1 KB copies per wave and tile
+  static constexpr int KS = D / 64;        // k-steps of S^T = K Q^T
+  static constexpr int DM = D / 32;        // 32-feature blocks of O^T
+  static_assert(D == 64 || D == 128, "head size");
+  static_assert(kDmaPerWave >= 1 && kTile % 4096 == 0, "tile must split into 1 KB copies per wave");
+  static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
+};
+
+// Chunk permutation of row r (16-byte chunks; kCpr per row, kRps rows per
+// 256-byte bank sweep).
+template <int D>
+struct Fp8Swizzle {
+  static constexpr int kCpr = D / 16;
+  static constexpr int kRps = 256 / D;
+  // K: the 16 rows one 16-lane read covers differ in (r % kRps, k(r)).
+  __device__ static int k(int r) { return ((r / kRps) & (kCpr / 2 - 1)) | (((r >> 4) & 1) * (kCpr / 2)); }
+  // V: 8 consecutive rows differ in (r % kRps, v(r)), and v(r) is even so
+  // the two adjacent chunks a 32-lane read covers stay apart.
+  __device__ static int v(int r) { return 2 * ((r / kRps) % (8 / kRps)); }
+};
+
+// Key (within a 32-key block) that row rho of the S^T product holds.
+__device__ __forceinline__ int kperm(int rho) {
+  return (((rho >> 2) & 1) << 4) | (((rho >> 3) & 3) << 2) | (rho & 3);
+}
+
+// This wave's share of a 64 x D byte tile starting at key j0, global -> LDS
+// (buffer_load ... lds, 1 KB per instruction in lane order); lane i loads the
+// global chunk that the permutation stores at its position.  Rows past the
+// head's end read as zero.
+template <int D, bool IS_K>
+__device__ __forceinline__ void dma_tile_fp8(__amdgpu_buffer_rsrc_t r, uint8_t* tile, int j0, int wq, int lane) {
+  using C = Fp8Cfg<D>;
+  using Z = Fp8Swizzle<D>;
+  constexpr int kRowsPerInst = 1024 / D;
+#pragma unroll
+  for (int i = 0; i < C::kDmaPerWave; ++i) {
+    const int inst = wq * C::kDmaPerWave + i;
+    const int row = inst * kRowsPerInst + lane / Z::kCpr;
+    const int chunk = (lane % Z::kCpr) ^ (IS_K ? Z::k(row) : Z::v(row));
+    const uint32_t goff = (uint32_t)((j0 + row) * D + 16 * chunk);
+    lds_copy16(r, goff, (uint32_t)(uintptr_t)(tile + inst * 1024));
+  }
+}
+
+// 32 bytes of a K row as an A operand: two 16-byte chunks.
+__device__ __forceinline__ i32x8 lds_k_operand(const uint8_t* p, int off0, int off1) {
+  const u32x4 a = *(const u32x4*)(p + off0);
+  const u32x4 b = *(const u32x4*)(p + off1);
+  return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// V^T A operand: four transposing reads of 8 keys each; p includes the
+// lane's offset, the reads sit 8, 32 and 40 rows further down.
+template <int D>
+__device__ __forceinline__ i32x8 lds_vt_operand(const uint8_t* p) {
+  const i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+  const i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8 * D));
+  const i32x2 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 32 * D));
+  const i32x2 d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 40 * D));
+  return (i32x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Keys past the end, and on the diagonal keys after the query, to -inf.
+// Register r of lane half lg in block mb holds key j0 + 32 mb + 16 lg + r.
+__device__ __forceinline__ void mask_tile_fp8(f32x16 (&s)[2], int j0, int qlim, int lg) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (j0 + 32 * mb + 16 * lg + r > qlim) s[mb][r] = -INFINITY;
+}
+
+// P = exp2(s * scale_log2 - m) for one tile, rounded to E4M3 and packed as
+// the B operand of the P V product (byte j = s[j / 16][j % 16]).  Returns
+// this lane's sum of P in fp32 (before rounding).
+__device__ __forceinline__ float tile_exp_fp8(const f32x16 (&s)[2], i32x8& pb, float m, float scale_log2) {
+  float rowsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int mb = w / 4, r0 = 4 * (w % 4);
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = fast_exp2(__builtin_fmaf(s[mb][r0 + e], scale_log2, -m));
+      rowsum += p[e];
+    }
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
+  }
+  return rowsum;
+}
+
+// Online-softmax step with the lazy reference (as in the bf16 kernel): keep
+// m unless some lane's tile sum of P against it exceeds kFp8PSumLimit (or
+// is not finite); then raise m to the tile max, rescale O and l, and redo
+// the exponentials.
+template <int D>
+__device__ __forceinline__ void softmax_step_fp8(const f32x16 (&s)[2], i32x8& pb, float& m_run, float& l_run,
+                                                 f32x16 (&oacc)[D / 32], float scale_log2) {
+  float rs = tile_exp_fp8(s, pb, m_run, scale_log2);
+  if (__ballot(!(rs <= kFp8PSumLimit))) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = max_with_lane_xor32(mx) * scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    rs = tile_exp_fp8(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
+  }
+  l_run += rs;
+}
+
+// One matrix phase: O^T += V^T(t) P^T(t) (D/32 products) then
+// S^T(t+1) = K(t+1) Q^T (2 KS products), one MFMA stream with the LDS
+// operands read L products ahead.
+template <int D, int L>
+__device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i32x8& pb, const uint8_t* Vs,
+                                                 const int (&voff)[D / 32], f32x16 (&s)[2], const uint8_t* Ks,
+                                                 const int (&koff)[D / 64][2], const i32x8 (&qb)[D / 64]) {
+  using C = Fp8Cfg<D>;
+  constexpr int kPv = C::DM;
+  constexpr int kAll = kPv + 2 * C::KS;
+  auto load = [&](int i) -> i32x8 {
+    if (i < kPv) return lds_vt_operand<D>(Vs + voff[i]);
+    const int j = i - kPv, ks = j / 2, mb = j % 2;
+    return lds_k_operand(Ks + 32 * mb * D, koff[ks][0], koff[ks][1]);
+  };
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
+  __builtin_amdgcn_s_setprio(1);
+  i32x8 ring[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) ring[i] = load(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kAll; ++i) {
+    const i32x8 a = ring[i % L];
+    if (i < kPv) {
+      oacc[i] = mfma32_fp8(a, pb, oacc[i]);
+    } else {
+      const int j = i - kPv, ks = j / 2, mb = j % 2;
+      s[mb] = mfma32_fp8(a, qb[ks], s[mb]);
+    }
+    if (i + L < kAll) ring[i % L] = load(i + L);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512)
+fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+                  __bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int num_qt, float scale_log2,
+                  float v_descale) {
+  using C = Fp8Cfg<D>;
+  using Z = Fp8Swizzle<D>;
+  constexpr int BN = C::BN;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int lane = tid & 63;
+  const int lc = lane & 31;
+  const int lg = lane >> 5;
+  const int wq = wave & 3;
+
+  const int bid = blockIdx.x;
+  const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
+  const int bh = bid % BH;
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rmine = make_rsrc((group == 0 ? K : V) + head_off, head_bytes);
+  auto kbuf = [&](int i) { return smem8 + i * C::kTile; };
+  auto vbuf = [&](int i) { return smem8 + (C::kBufs + i) * C::kTile; };
+  auto copy_tile = [&](int tile, int buf) {
+    if (group == 0) dma_tile_fp8<D, true>(rmine, kbuf(buf), tile * BN, wq, lane);
+    else dma_tile_fp8<D, false>(rmine, vbuf(buf), tile * BN, wq, lane);
+  };
+
+  // Lane offsets.  K: row kperm(lc) of each 32-key block, chunks
+  // 4 ks + 2 lg and 4 ks + 2 lg + 1.  V^T: 16-lane group (G = bit 4) reads
+  // rows 16 lg + 0..7 (+8, +32, +40) of chunk 2 dm + G, lane s = lane % 16
+  // addressing row s / 2, bytes 8 (s % 2).
+  int koff[C::KS][2], voff[C::DM];
+  {
+    const int kr = kperm(lc);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) koff[ks][p] = kr * D + 16 * ((4 * ks + 2 * lg + p) ^ Z::k(kr));
+    const int sl = lane & 15, G = (lane >> 4) & 1;
+    const int row = 16 * lg + (sl >> 1);
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm) voff[dm] = row * D + 16 * ((2 * dm + G) ^ Z::v(row)) + 8 * (sl & 1);
+  }
+
+  const int q_wave0 = qt * C::BM + wave * 32;
+  const int q_idx = q_wave0 + lc;
+
+  // Q codes as the B operand: lane holds Q[q][64 ks + 32 lg .. +31].
+  i32x8 qb[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const uint32_t off = (uint32_t)(q_idx * D + 64 * ks + 32 * lg);
+    const u32x4 a = bload128(rq, off), b = bload128(rq, off + 16);
+    qb[ks] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+
+  f32x16 oacc[C::DM];
+#pragma unroll
+  for (int i = 0; i < C::DM; ++i) oacc[i] = (f32x16){};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int q_tile_end = min(N, (qt + 1) * C::BM);
+  const int key_end = CAUSAL ? q_tile_end : N;
+  const int num_kt = (key_end + BN - 1) / BN;
+  const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
+  auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
+
+  if (num_kt > 0) copy_tile(0, 0);
+  if (num_kt > 1) copy_tile(1, 1);
+  wait_vmem_all();
+  __syncthreads();
+
+  f32x16 s[2];
+  i32x8 pb;
+  if (num_kt > 0) {
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = mfma32_fp8(lds_k_operand(kbuf(0) + 32 * mb * D, koff[ks][0], koff[ks][1]), qb[ks], s[mb]);
+    if (masked(0)) mask_tile_fp8(s, 0, qlim, lg);
+    softmax_step_fp8<D>(s, pb, m_run, l_run, oacc, scale_log2);
+  }
+
+  // Ping-pong and copy schedule as in the bf16 kernel: group 1 runs one
+  // barrier interval behind group 0; tile t + 2 is copied into buffer
+  // (t + 2) % 3 during step t and waited for at the end of the step's
+  // vector phase.
+  if (group == 1) __syncthreads();
+  int b_cur = 0;
+  for (int t = 0; t < num_kt; ++t) {
+    const int b_next = b_cur == 2 ? 0 : b_cur + 1;
+    const int b_copy = b_cur == 0 ? 2 : b_cur - 1;
+    if (t + 2 < num_kt) copy_tile(t + 2, b_copy);
+    matrix_phase_fp8<D, 3>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
+    __syncthreads();
+    if (t + 1 < num_kt) {
+      if (masked(t + 1)) mask_tile_fp8(s, (t + 1) * BN, qlim, lg);
+      softmax_step_fp8<D>(s, pb, m_run, l_run, oacc, scale_log2);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    b_cur = b_next;
+  }
+  if (group == 0) __syncthreads();
+
+  // O = O^T / l * v_descale as bf16; LSE = m ln 2 + ln l.
+  const float l_tot = sum_with_lane_xor32(l_run);
+  const float f = l_tot > 0.f ? v_descale / l_tot : 0.f;
+  if (q_idx < N) {
+    __bf16* orow = O + head_off + (size_t)q_idx * D;
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * f, oacc[dm][4 * i + 1] * f),
+                   pack_bf16x2(oacc[dm][4 * i + 2] * f, oacc[dm][4 * i + 3] * f)};
+        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * lg) = w;
+      }
+    if (LSE != nullptr && lg == 0)
+      LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fp8_d(const FwdFp8Args& a) {
+  using C = Fp8Cfg<D>;
+  const int BH = a.B * a.H;
+  const int num_qt = (a.N + C::BM - 1) / C::BM;
+  auto kern = fa_fwd_fp8_kernel<D, CAUSAL>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), C::kLdsBytes, a.stream, (const uint8_t*)a.q,
+                     (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o, a.lse, a.N, BH, num_qt,
+                     a.scale * a.q_descale * a.k_descale * kLog2e, a.v_descale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const FwdFp8Args& a) {
+  if (a.d == 64) return a.causal ? launch_fp8_d<64, true>(a) : launch_fp8_d<64, false>(a);
+  return a.causal ? launch_fp8_d<128, true>(a) : launch_fp8_d<128, false>(a);
+}
+
+}  // namespace fa

@@ -24,6 +24,19 @@ struct FwdArgs {
   const unsigned char* bmask;   // block-sparse mask [B, H, nb, nb], or null (dense)
 };
 
+struct FwdFp8Args {
+  const void* q;   // E4M3 codes [B, H, N, d]
+  const void* k;
+  const void* v;
+  float q_descale, k_descale, v_descale;
+  void* o;         // bf16 [B, H, N, d]
+  float* lse;      // [B, H, N] or null
+  int B, H, N, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -59,6 +72,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const FwdFp8Args& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 size_t decode_workspace_bytes(int B, int H, int Nk, int d);   // valid sizes only

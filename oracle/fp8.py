@@ -59,20 +59,21 @@ def attention_forward_fp8_head(q8, k8, v8, q_descale, k_descale, v_descale, scal
     return attention_forward_head(q, k, v, scale=scale, causal=causal, rows=rows)
 
 
-def attention_weights_fp8_head(q8, k8, q_descale, k_descale, scale=None, causal=False):
-    """Softmax weights P [N, N] (row i: the weights query i gives each key) of
-    one head stored as E4M3 codes, from the safe softmax of each scaled,
-    masked score row.  Small N only (the whole matrix is formed); the tests
-    use it to bound the effect of rounding P."""
+def attention_weights_fp8_head(q8, k8, q_descale, k_descale, scale=None, causal=False, rows=None):
+    """Softmax weights [len(rows), N] (row i: the weights query rows[i] gives
+    each key) of one head stored as E4M3 codes, from the safe softmax of each
+    scaled, masked score row.  The tests use it to bound the effect of
+    rounding the weights."""
     q = dequantize(q8, q_descale)
     k = dequantize(k8, k_descale)
     if scale is None:
         scale = default_scale(q.shape[-1])
-    n = q.shape[0]
-    w = np.zeros((n, k.shape[0]), dtype=np.float64)
-    for i in range(n):
+    if rows is None:
+        rows = np.arange(q.shape[0])
+    w = np.zeros((len(rows), k.shape[0]), dtype=np.float64)
+    for n, i in enumerate(rows):
         s = scale * (k @ q[i])
         if causal:
             s[i + 1:] = -np.inf
-        w[i] = safe_softmax(s)[0]
+        w[n] = safe_softmax(s)[0]
     return w

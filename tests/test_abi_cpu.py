@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
                             "flash_attn_bwd_workspace_size", "flash_attn_status_string",
                             "flash_attn_last_hip_error", "flash_attn_fwd_blocksparse",
                             "flash_attn_bwd_blocksparse", "flash_attn_decode",
-                            "flash_attn_decode_workspace_size"])
+                            "flash_attn_decode_workspace_size", "flash_attn_fwd_fp8"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -215,3 +215,29 @@ def test_decode_workspace_size():
     assert f(16, 32, 8192, 128) > 0 and f(16, 32, 8192, 128) % 256 == 0
     assert f(1, 1, 1, 64) > 0
     assert f(0, 1, 64, 64) == 0 and f(1, 1, 64, 96) == 0
+
+
+def fwd_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=0.01, kd=0.01, vd=0.01, o=FAKE, lse=FAKE, B=1, H=1, N=64, d=128,
+             scale=0.125, causal=0, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_fwd_fp8(a["q"], a["k"], a["v"], a["qd"], a["kd"], a["vd"], a["o"], a["lse"],
+                                             a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(qd=0.0), binding.FA_ERR_INVALID_ARG),
+    (dict(kd=-1.0), binding.FA_ERR_INVALID_ARG),
+    (dict(vd=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(vd=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), binding.FA_ERR_INVALID_ARG),
+    (dict(v=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+])
+def test_fp8_forward_rejects_bad_arguments(kw, code):
+    assert fwd_fp8(**kw) == code

@@ -84,6 +84,8 @@ def _attention_checks(mod):
         if causal:
             assert np.all(np.triu(w, 1) == 0)
         np.testing.assert_allclose(w @ (lib["v"] * ds["v"]), o, rtol=1e-12, atol=1e-15)
+        ws = mod.attention_weights_fp8_head(codes["q"], codes["k"], ds["q"], ds["k"], causal=causal, rows=[6, 2])
+        np.testing.assert_array_equal(ws, w[[6, 2]])
 
 
 def test_decoder_pins():
