@@ -27,9 +27,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOP/s and % of MI355X bf16 MFMA peak at N=4K,d=128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published figure
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published figure
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["io_aware_tiled_attn_amd/csrc/fa_fwd.hip", "io_aware_tiled_attn_amd/csrc/fa_bwd.hip",
+                  "io_aware_tiled_attn_amd/csrc/fa_fwd_fp8.hip",
                   "io_aware_tiled_attn_amd/csrc/fa_decode.hip", "io_aware_tiled_attn_amd/csrc/fa_common.h"]
 
 
@@ -44,6 +46,8 @@ def parse_args():
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the KV-cache decoding step reported beside the dense one")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 forward reported beside the dense step")
     ap.add_argument("--no-blocksparse", action="store_true",
                     help="skip the block-sparse step reported beside the dense one")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -188,6 +192,48 @@ def blocksparse_step(q, k, v, do, o, lse, dq, dk, dv, ws, stream, dense_ms, warm
         "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
         "unit": "TFLOP/s on kept blocks",
         "speedup_vs_dense_causal_step": round(dense_ms / ms, 3),
+    }
+
+
+def fp8_step(warmup, steps):
+    """FP8 forward on the N=4096, d=128 causal shape: the same seeded draws
+    quantized to E4M3 with one descale per tensor.  FLOPs are the forward's
+    (4 N^2 d per head, halved by the causal mask), against the FP8 peak."""
+    import numpy as np
+    import torch
+    import io_aware_tiled_attn_amd as fa
+    from io_aware_tiled_attn_amd import workloads as wl
+    w = wl.FP8_WORKLOAD
+    inp = wl.fp8_inputs(w.shape, w.seed)
+    q, k, v = (torch.from_numpy(inp[n]).cuda() for n in ("q", "k", "v"))
+    o = torch.empty(w.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ds = (inp["q_descale"], inp["k_descale"], inp["v_descale"])
+
+    def run():
+        fa.flash_attn_fwd_fp8(q, k, v, *ds, causal=w.causal, out=o, lse=lse)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    f_fwd = flops(w)[0]
+    tf = f_fwd / (ms * 1e-3) / 1e12
+    return {
+        "workload": "%s: B=%d H=%d N=%d d=%d, E4M3 inputs with per-tensor descales, bf16 output, causal"
+                    % (w.name, w.B, w.H, w.N, w.d),
+        "ms": round(ms, 4),
+        "tflops": round(tf, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic("fa_fwd_fp8_kernel", w.name)},
     }
 
 
@@ -367,6 +413,9 @@ def main():
                                                  torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv),
                                                  ws, stream, ms_per_step, max(5, args.warmup // 2),
                                                  max(10, args.steps // 2))
+    if not args.no_fp8:
+        print("[bench] FP8 forward", file=sys.stderr, flush=True)
+        result["fp8_forward"] = fp8_step(max(5, args.warmup // 2), args.steps)
     if not args.no_decode:
         print("[bench] decoding step", file=sys.stderr, flush=True)
         result["decode"] = decode_step(max(5, args.warmup // 2), args.steps)

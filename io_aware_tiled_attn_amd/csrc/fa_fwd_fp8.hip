@@ -50,12 +50,13 @@ __device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int D>
+template <int D, int BN>
 struct Fp8Cfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int BM = kWaves * 32;
-  static constexpr int BN = 64;            // keys per tile: the k of one P V product
+  static constexpr int NB = BN / 32;       // 32-key blocks of S^T per tile
+  static constexpr int NC = BN / 64;       // 64-key chunks per tile: the k of one P V product
   static constexpr int kTile = BN * D;     // bytes of one K or V tile
   static constexpr int kBufs = 3;
   static constexpr int kLdsBytes = 2 * kBufs * kTile;
@@ -63,6 +64,11 @@ struct Fp8Cfg {
   static constexpr int KS = D / 64;        // k-steps of S^T = K Q^T
   static constexpr int DM = D / 32;        // 32-feature blocks of O^T
   static_assert(D == 64 || D == 128, "head size");
+  // 64-key tiles only.  A 128-key build of this code measured slower (1418
+  // against 1490 TFLOP/s at N = 4096, d = 128, causal), and its output
+  // changed from run to run and differed from the 64-key build's far beyond
+  // rounding; the cause was not found, so that width stays disabled.
+  static_assert(BN == 64, "key tile");
   static_assert(kDmaPerWave >= 1 && kTile % 4096 == 0, "tile must split into 1 KB copies per wave");
   static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
 };
@@ -85,13 +91,13 @@ __device__ __forceinline__ int kperm(int rho) {
   return (((rho >> 2) & 1) << 4) | (((rho >> 3) & 3) << 2) | (rho & 3);
 }
 
-// This wave's share of a 64 x D byte tile starting at key j0, global -> LDS
+// This wave's share of a BN x D byte tile starting at key j0, global -> LDS
 // (buffer_load ... lds, 1 KB per instruction in lane order); lane i loads the
 // global chunk that the permutation stores at its position.  Rows past the
 // head's end read as zero.
-template <int D, bool IS_K>
+template <int D, int BN, bool IS_K>
 __device__ __forceinline__ void dma_tile_fp8(__amdgpu_buffer_rsrc_t r, uint8_t* tile, int j0, int wq, int lane) {
-  using C = Fp8Cfg<D>;
+  using C = Fp8Cfg<D, BN>;
   using Z = Fp8Swizzle<D>;
   constexpr int kRowsPerInst = 1024 / D;
 #pragma unroll
@@ -124,31 +130,37 @@ __device__ __forceinline__ i32x8 lds_vt_operand(const uint8_t* p) {
 
 // Keys past the end, and on the diagonal keys after the query, to -inf.
 // Register r of lane half lg in block mb holds key j0 + 32 mb + 16 lg + r.
-__device__ __forceinline__ void mask_tile_fp8(f32x16 (&s)[2], int j0, int qlim, int lg) {
+template <int BN>
+__device__ __forceinline__ void mask_tile_fp8(f32x16 (&s)[BN / 32], int j0, int qlim, int lg) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (j0 + 32 * mb + 16 * lg + r > qlim) s[mb][r] = -INFINITY;
 }
 
 // P = exp2(s * scale_log2 - m) for one tile, rounded to E4M3 and packed as
-// the B operand of the P V product (byte j = s[j / 16][j % 16]).  Returns
-// this lane's sum of P in fp32 (before rounding).
-__device__ __forceinline__ float tile_exp_fp8(const f32x16 (&s)[2], i32x8& pb, float m, float scale_log2) {
+// the B operands of the P V products (64-key chunk c: byte j =
+// s[2 c + j / 16][j % 16]).  Returns this lane's sum of P in fp32 (before
+// rounding).
+template <int BN>
+__device__ __forceinline__ float tile_exp_fp8(const f32x16 (&s)[BN / 32], i32x8 (&pb)[BN / 64], float m,
+                                              float scale_log2) {
   float rowsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const int mb = w / 4, r0 = 4 * (w % 4);
-    float p[4];
+  for (int c = 0; c < BN / 64; ++c)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] = fast_exp2(__builtin_fmaf(s[mb][r0 + e], scale_log2, -m));
-      rowsum += p[e];
+    for (int w = 0; w < 8; ++w) {
+      const int mb = 2 * c + w / 4, r0 = 4 * (w % 4);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(s[mb][r0 + e], scale_log2, -m));
+        rowsum += p[e];
+      }
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      pb[c][w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
     }
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-    pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
-  }
   return rowsum;
 }
 
@@ -156,14 +168,14 @@ __device__ __forceinline__ float tile_exp_fp8(const f32x16 (&s)[2], i32x8& pb, f
 // m unless some lane's tile sum of P against it exceeds kFp8PSumLimit (or
 // is not finite); then raise m to the tile max, rescale O and l, and redo
 // the exponentials.
-template <int D>
-__device__ __forceinline__ void softmax_step_fp8(const f32x16 (&s)[2], i32x8& pb, float& m_run, float& l_run,
-                                                 f32x16 (&oacc)[D / 32], float scale_log2) {
-  float rs = tile_exp_fp8(s, pb, m_run, scale_log2);
+template <int D, int BN>
+__device__ __forceinline__ void softmax_step_fp8(const f32x16 (&s)[BN / 32], i32x8 (&pb)[BN / 64], float& m_run,
+                                                 float& l_run, f32x16 (&oacc)[D / 32], float scale_log2) {
+  float rs = tile_exp_fp8<BN>(s, pb, m_run, scale_log2);
   if (__ballot(!(rs <= kFp8PSumLimit))) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
     mx = max_with_lane_xor32(mx) * scale_log2;
@@ -173,28 +185,29 @@ __device__ __forceinline__ void softmax_step_fp8(const f32x16 (&s)[2], i32x8& pb
     l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-    rs = tile_exp_fp8(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
+    rs = tile_exp_fp8<BN>(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
   }
   l_run += rs;
 }
 
-// One matrix phase: O^T += V^T(t) P^T(t) (D/32 products) then
-// S^T(t+1) = K(t+1) Q^T (2 KS products), one MFMA stream with the LDS
+// One matrix phase: O^T += V^T(t) P^T(t) (NC DM products) then
+// S^T(t+1) = K(t+1) Q^T (NB KS products), one MFMA stream with the LDS
 // operands read L products ahead.
-template <int D, int L>
-__device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i32x8& pb, const uint8_t* Vs,
-                                                 const int (&voff)[D / 32], f32x16 (&s)[2], const uint8_t* Ks,
+template <int D, int BN, int L>
+__device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i32x8 (&pb)[BN / 64],
+                                                 const uint8_t* Vs, const int (&voff)[D / 32],
+                                                 f32x16 (&s)[BN / 32], const uint8_t* Ks,
                                                  const int (&koff)[D / 64][2], const i32x8 (&qb)[D / 64]) {
-  using C = Fp8Cfg<D>;
-  constexpr int kPv = C::DM;
-  constexpr int kAll = kPv + 2 * C::KS;
+  using C = Fp8Cfg<D, BN>;
+  constexpr int kPv = C::NC * C::DM;
+  constexpr int kAll = kPv + C::NB * C::KS;
   auto load = [&](int i) -> i32x8 {
-    if (i < kPv) return lds_vt_operand<D>(Vs + voff[i]);
-    const int j = i - kPv, ks = j / 2, mb = j % 2;
+    if (i < kPv) return lds_vt_operand<D>(Vs + voff[i % C::DM] + 64 * (i / C::DM) * D);
+    const int j = i - kPv, ks = j / C::NB, mb = j % C::NB;
     return lds_k_operand(Ks + 32 * mb * D, koff[ks][0], koff[ks][1]);
   };
-  s[0] = (f32x16){};
-  s[1] = (f32x16){};
+#pragma unroll
+  for (int mb = 0; mb < C::NB; ++mb) s[mb] = (f32x16){};
   __builtin_amdgcn_s_setprio(1);
   i32x8 ring[L];
 #pragma unroll
@@ -204,9 +217,9 @@ __device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i
   for (int i = 0; i < kAll; ++i) {
     const i32x8 a = ring[i % L];
     if (i < kPv) {
-      oacc[i] = mfma32_fp8(a, pb, oacc[i]);
+      oacc[i % C::DM] = mfma32_fp8(a, pb[i / C::DM], oacc[i % C::DM]);
     } else {
-      const int j = i - kPv, ks = j / 2, mb = j % 2;
+      const int j = i - kPv, ks = j / C::NB, mb = j % C::NB;
       s[mb] = mfma32_fp8(a, qb[ks], s[mb]);
     }
     if (i + L < kAll) ring[i % L] = load(i + L);
@@ -215,14 +228,15 @@ __device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, bool CAUSAL>
+}  // namespace
+
+template <int D, int BN, bool CAUSAL>
 __global__ void __launch_bounds__(512)
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                   __bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int num_qt, float scale_log2,
                   float v_descale) {
-  using C = Fp8Cfg<D>;
+  using C = Fp8Cfg<D, BN>;
   using Z = Fp8Swizzle<D>;
-  constexpr int BN = C::BN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
 
   const int tid = threadIdx.x;
@@ -243,8 +257,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   auto kbuf = [&](int i) { return smem8 + i * C::kTile; };
   auto vbuf = [&](int i) { return smem8 + (C::kBufs + i) * C::kTile; };
   auto copy_tile = [&](int tile, int buf) {
-    if (group == 0) dma_tile_fp8<D, true>(rmine, kbuf(buf), tile * BN, wq, lane);
-    else dma_tile_fp8<D, false>(rmine, vbuf(buf), tile * BN, wq, lane);
+    if (group == 0) dma_tile_fp8<D, BN, true>(rmine, kbuf(buf), tile * BN, wq, lane);
+    else dma_tile_fp8<D, BN, false>(rmine, vbuf(buf), tile * BN, wq, lane);
   };
 
   // Lane offsets.  K: row kperm(lc) of each 32-key block, chunks
@@ -293,18 +307,18 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   wait_vmem_all();
   __syncthreads();
 
-  f32x16 s[2];
-  i32x8 pb;
+  f32x16 s[C::NB];
+  i32x8 pb[C::NC];
   if (num_kt > 0) {
-    s[0] = (f32x16){};
-    s[1] = (f32x16){};
+#pragma unroll
+    for (int mb = 0; mb < C::NB; ++mb) s[mb] = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NB; ++mb)
         s[mb] = mfma32_fp8(lds_k_operand(kbuf(0) + 32 * mb * D, koff[ks][0], koff[ks][1]), qb[ks], s[mb]);
-    if (masked(0)) mask_tile_fp8(s, 0, qlim, lg);
-    softmax_step_fp8<D>(s, pb, m_run, l_run, oacc, scale_log2);
+    if (masked(0)) mask_tile_fp8<BN>(s, 0, qlim, lg);
+    softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
   }
 
   // Ping-pong and copy schedule as in the bf16 kernel: group 1 runs one
@@ -317,11 +331,11 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;
     const int b_copy = b_cur == 0 ? 2 : b_cur - 1;
     if (t + 2 < num_kt) copy_tile(t + 2, b_copy);
-    matrix_phase_fp8<D, 3>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
+    matrix_phase_fp8<D, BN, 3>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     if (t + 1 < num_kt) {
-      if (masked(t + 1)) mask_tile_fp8(s, (t + 1) * BN, qlim, lg);
-      softmax_step_fp8<D>(s, pb, m_run, l_run, oacc, scale_log2);
+      if (masked(t + 1)) mask_tile_fp8<BN>(s, (t + 1) * BN, qlim, lg);
+      softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     }
     wait_vmem_all();
     __syncthreads();
@@ -348,19 +362,18 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_fp8_d(const FwdFp8Args& a) {
-  using C = Fp8Cfg<D>;
+static hipError_t launch_fp8_d(const FwdFp8Args& a) {
+  constexpr int BN = 64;
+  using C = Fp8Cfg<D, BN>;
   const int BH = a.B * a.H;
   const int num_qt = (a.N + C::BM - 1) / C::BM;
-  auto kern = fa_fwd_fp8_kernel<D, CAUSAL>;
+  auto kern = fa_fwd_fp8_kernel<D, BN, CAUSAL>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), C::kLdsBytes, a.stream, (const uint8_t*)a.q,
                      (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o, a.lse, a.N, BH, num_qt,
                      a.scale * a.q_descale * a.k_descale * kLog2e, a.v_descale);
   return hipGetLastError();
 }
-
-}  // namespace
 
 hipError_t launch_fwd_fp8(const FwdFp8Args& a) {
   if (a.d == 64) return a.causal ? launch_fp8_d<64, true>(a) : launch_fp8_d<64, false>(a);
