@@ -238,6 +238,31 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     n_steps = __builtin_amdgcn_readfirstlane(slist[0]);
   }
   auto step_at = [&](int j) { return SPARSE ? slist[1 + j] : qt_begin + j; };
+  // dQ partials of the previous step, added to the accumulator with atomics
+  // spread over the next step's matrix and vector work (four at a time) so
+  // that their issue overlaps computation instead of stalling the wave.
+  f32x16 dq_pend[C::kDqPerWave];
+  int q0_pend = -1;
+  int qbk[C::kDqPerWave], dmk[C::kDqPerWave];
+#pragma unroll
+  for (int j = 0; j < C::kDqPerWave; ++j) {
+    const int blk = wave * C::kDqPerWave + j;
+    qbk[j] = blk / (D / 32);
+    dmk[j] = blk % (D / 32);
+  }
+  constexpr int kPendParts = 8;
+  constexpr int kPendPerPart = C::kDqPerWave * 16 / kPendParts;
+  static_assert(C::kDqPerWave * 16 % kPendParts == 0, "atomic spreading");
+  auto flush_pending = [&](int part) {
+    if (q0_pend >= 0) {
+#pragma unroll
+      for (int t = 0; t < kPendPerPart; ++t) {
+        const int idx = part * kPendPerPart + t, j = idx / 16, r = idx % 16;
+        const int q = q0_pend + 32 * qbk[j] + 8 * (r >> 2) + 4 * lg + (r & 3);
+        batomic_add(h.dq, (uint32_t)(q * D + 32 * dmk[j] + lc) * 4u, dq_pend[j][r]);
+      }
+    }
+  };
   BwdStage<D> st;
   if (n_steps > 0) {
     bwd_load_stage<D>(st, h, step_at(0) * C::BM, N, tid);
@@ -360,6 +385,7 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     for (int j = 0; j < 4; ++j) {
       score_steps(1, min(KS, j * KSC), min(KS, (j + 1) * KSC));
       vector_group(0, j);
+      flush_pending(j);
       __builtin_amdgcn_sched_barrier(0);
     }
     mask_scores(1);
@@ -368,6 +394,7 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     for (int j = 0; j < 4; ++j) {
       update_pairs(0, min(2 * DM, j * UPC), min(2 * DM, (j + 1) * UPC));
       vector_group(1, j);
+      flush_pending(4 + j);
       __builtin_amdgcn_sched_barrier(0);
     }
     update_pairs(1, 0, 2 * DM);
@@ -379,14 +406,8 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     // summing over all keys; independent blocks of a wave interleave.
     {
       f32x16 acc[C::kDqPerWave];
-      int qbk[C::kDqPerWave], dmk[C::kDqPerWave];
 #pragma unroll
-      for (int j = 0; j < C::kDqPerWave; ++j) {
-        const int blk = wave * C::kDqPerWave + j;
-        qbk[j] = blk / (D / 32);
-        dmk[j] = blk % (D / 32);
-        acc[j] = (f32x16){};
-      }
+      for (int j = 0; j < C::kDqPerWave; ++j) acc[j] = (f32x16){};
       const __bf16* dsp = dSt + tr_off_n;
       const __bf16* dslp = dSt_lo + tr_off_n;
       const __bf16* ktp = Kt + kt_lane_off;
@@ -404,14 +425,12 @@ fa_bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
         }
       }
 #pragma unroll
-      for (int j = 0; j < C::kDqPerWave; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + 32 * qbk[j] + 8 * (r >> 2) + 4 * lg + (r & 3);
-          batomic_add(h.dq, (uint32_t)(q * D + 32 * dmk[j] + lc) * 4u, acc[j][r]);
-        }
+      for (int j = 0; j < C::kDqPerWave; ++j) dq_pend[j] = acc[j];
+      q0_pend = q0;
     }
   }
+#pragma unroll
+  for (int part = 0; part < kPendParts; ++part) flush_pending(part);
 
   // dK = scale dK^T, dV = dV^T, stored as bf16 rows of this lane's key.
   if (key < N) {
