@@ -59,8 +59,10 @@ __host__ __device__ inline int decode_splits(int BH, int Nk) {
   return s < 1 ? 1 : s;
 }
 
+// Four waves per SIMD (at most 128 registers each): decode_splits sizes the
+// launch for exactly that many waves, so they all run in one round.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 fa_decode_split_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                        float* __restrict__ part_o, float* __restrict__ part_lse, int BH, int Nq, int Nk,
                        int n_split, float scale_log2) {
