@@ -92,7 +92,7 @@ template <int D>
 struct BwdStage {
   u32x4 q[BwdCfg<D>::kChunksPerThread];
   u32x4 g[BwdCfg<D>::kChunksPerThread];
-  float lse2;   // LSE * log2(e) for one row (threads 0..BM-1), +inf past N
+  float lse;    // LSE of one row as loaded (threads 0..BM-1), +inf past N
   float dlt;    // D for one row (threads BM..2BM-1)
 };
 
@@ -113,12 +113,12 @@ __device__ __forceinline__ void bwd_load_stage(BwdStage<D>& st, const BwdHead& h
     st.q[i] = bload128(h.q, off);
     st.g[i] = bload128(h.g, off);
   }
-  // LSE * log2(e) (+inf past N, and for rows that saw no key at all,
-  // LSE = -inf, so P = 0 there) and D (0 past N).
+  // LSE (+inf past N) and D (0 past N), kept as loaded: nothing here
+  // waits for the loads, which complete behind the step's computation and
+  // are first used in bwd_store_stage.
   if (tid < C::BM) {
     const int q = q0 + tid;
-    const float l = q < N ? bload32f(h.lse, (uint32_t)q * 4u) : INFINITY;
-    st.lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    st.lse = q < N ? bload32f(h.lse, (uint32_t)q * 4u) : INFINITY;
   } else if (tid < 2 * C::BM) {
     st.dlt = bload32f(h.dlt, (uint32_t)(q0 + tid - C::BM) * 4u);
   }
@@ -138,7 +138,9 @@ __device__ __forceinline__ void bwd_store_stage(const BwdStage<D>& st, char* sta
     *(u32x4*)(Qs + row * C::kRowPitch + col) = st.q[i];
     *(u32x4*)(Gs + row * C::kRowPitch + col) = st.g[i];
   }
-  if (tid < C::BM) Ls[tid] = st.lse2;
+  // LSE * log2(e); rows that saw no key at all (LSE = -inf) get +inf, so
+  // P = 0 there.
+  if (tid < C::BM) Ls[tid] = st.lse == -INFINITY ? INFINITY : st.lse * kLog2e;
   else if (tid < 2 * C::BM) Ds[tid - C::BM] = st.dlt;
 }
 
