@@ -269,6 +269,20 @@ def decode_step(warmup, steps):
     kv_bytes = 2.0 * w.B * w.H * w.Nk * w.d * 2
     qo_bytes = 2.0 * w.B * w.H * w.Nq * w.d * 2 + 4.0 * w.B * w.H * w.Nq
     gbs = (kv_bytes + qo_bytes) / (ms * 1e-3) / 1e9
+    # Context for the roofline: what a plain device-to-device copy (HIP
+    # runtime, 1 GiB read + 1 GiB written) sustains on this GPU.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * src.numel() / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
+    del src, dst
     t_split = measured_traffic("fa_decode_split_kernel", w.name)
     t_merge = measured_traffic("fa_decode_merge_kernel", w.name)
     traffic = t_split + t_merge if t_split is not None and t_merge is not None else None
@@ -280,6 +294,7 @@ def decode_step(warmup, steps):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "bytes_per_launch": int(kv_bytes + qo_bytes), "traffic": traffic},
+        "device_copy_gbs": round(copy_gbs, 1),
     }
 
 

@@ -203,3 +203,14 @@ def fp8_inputs(shape, seed):
 # quantized from the same draws (seed 3) as the bf16 workload.
 FP8_WORKLOAD = Workload("fp8_n4k_d128_causal", 4, 32, 4096, 128, "fp8", True, False, 3,
                         "FP8 (E4M3, per-tensor descale) B4 H32 N4096 d128, causal, forward")
+
+
+def gpu_normal_bf16(shape, seed, device="cuda"):
+    """N(0, 1) values rounded to bf16, drawn on the GPU by torch's seeded
+    Philox generator: for tensors too large to draw on the host in a test
+    (the inputs near the library's element limit).  Tests copy the heads they
+    check back to the host and give those exact values to the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
