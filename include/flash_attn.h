@@ -253,6 +253,28 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
                        int B, int H, int N, int d,
                        float scale, int causal, void* stream);
 
+/*
+ * Merge of two partial attention results over disjoint sets of keys, the
+ * online-softmax update rule of vibeengines.com "FlashAttention, explained"
+ * ("Tiling and the online softmax") applied to whole blocks in LSE form:
+ *     L = ln(e^La + e^Lb),   O = e^(La - L) Oa + e^(Lb - L) Ob,
+ * row by row.  It is the step a sequence-parallel (ring) schedule repeats
+ * as key/value chunks visit the device that holds some query rows: each
+ * chunk's forward result (O, LSE from flash_attn_fwd) is folded into a
+ * running result.  Start the running result at o_acc = 0, lse_acc = -inf.
+ * A row with LSE = -inf on both sides (no key yet) stays 0 / -inf.
+ *   o_acc    : float32 [rows, d], read and written (the running output).
+ *   lse_acc  : float32 [rows], read and written.
+ *   o_part   : bf16 [rows, d], read.   lse_part : float32 [rows], read.
+ *   o_out    : bf16 [rows, d], written with the merged output (may be NULL).
+ *   rows     : number of rows (B * H * N for [B, H, N, d] tensors).
+ * d in {64, 128} (else FA_ERR_UNSUPPORTED); null inputs, rows < 1,
+ * rows * d >= 2^31 or a misaligned o_acc / o_part / o_out give
+ * FA_ERR_INVALID_ARG.  o_out must not alias the inputs.
+ */
+int flash_attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
+                     void* o_out, long long rows, int d, void* stream);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char* flash_attn_status_string(int status);
 

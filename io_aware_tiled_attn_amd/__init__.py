@@ -16,6 +16,7 @@ __all__ = [
     "flash_attn_fwd_blocksparse",
     "flash_attn_bwd_blocksparse",
     "flash_attn_decode",
+    "flash_attn_merge",
     "flash_attn_decode_workspace_size",
     "flash_attn_bwd_workspace_size",
     "flash_attn_status_string",

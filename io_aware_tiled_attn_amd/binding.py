@@ -74,6 +74,8 @@ def _raw():
     lib.flash_attn_decode.restype = i
     lib.flash_attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, f, i, vp]
     lib.flash_attn_fwd_fp8.restype = i
+    lib.flash_attn_merge.argtypes = [vp, vp, vp, vp, vp, ctypes.c_longlong, i, vp]
+    lib.flash_attn_merge.restype = i
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     lib.flash_attn_last_hip_error.argtypes = []
@@ -193,6 +195,28 @@ def flash_attn_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, s
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd_fp8")
     return out, lse
+
+
+def flash_attn_merge(o_acc, lse_acc, o_part, lse_part, out=None, stream=None):
+    """Fold a partial result (o_part bf16 [..., N, d], lse_part fp32 [..., N])
+    over another set of keys into the running result (o_acc fp32, lse_acc
+    fp32, same shapes), in place; out (bf16, optional) receives the merged O.
+    Returns out (or None)."""
+    torch = _torch()
+    shape = tuple(o_part.shape)
+    d = shape[-1]
+    rows = o_part.numel() // d
+    _check(o_acc, "o_acc", torch.float32, shape)
+    _check(lse_acc, "lse_acc", torch.float32, shape[:-1])
+    _check(o_part, "o_part", torch.bfloat16, shape)
+    _check(lse_part, "lse_part", torch.float32, shape[:-1])
+    if out is not None:
+        _check(out, "out", torch.bfloat16, shape)
+    st = _raw().flash_attn_merge(o_acc.data_ptr(), lse_acc.data_ptr(), o_part.data_ptr(), lse_part.data_ptr(),
+                                 None if out is None else out.data_ptr(), rows, d, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_merge")
+    return out
 
 
 def flash_attn_bwd_ex(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, stream=None,

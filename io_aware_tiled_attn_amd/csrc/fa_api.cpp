@@ -112,6 +112,16 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v, float q_desc
   return hip_status(fa::launch_fwd_fp8(a));
 }
 
+int flash_attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part, void* o_out,
+                     long long rows, int d, void* stream) {
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return FA_ERR_INVALID_ARG;
+  if (rows < 1 || d < 1 || rows * d > kMaxElems) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(o_acc) || !aligned16(o_part) || (o_out && !aligned16(o_out))) return FA_ERR_INVALID_ARG;
+  fa::MergeArgs a{o_acc, lse_acc, o_part, lse_part, o_out, (long)rows, d, (hipStream_t)stream};
+  return hip_status(fa::launch_merge(a));
+}
+
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   if ((long long)B * H * N * d > kMaxElems) return 0;

@@ -71,7 +71,19 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+struct MergeArgs {
+  float* o_acc;          // fp32 [rows, d], in/out
+  float* lse_acc;        // fp32 [rows], in/out
+  const void* o_part;    // bf16 [rows, d]
+  const float* lse_part; // fp32 [rows]
+  void* o_out;           // bf16 [rows, d] or null
+  long rows;
+  int d;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_fwd_fp8(const FwdFp8Args& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);

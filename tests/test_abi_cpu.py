@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
                             "flash_attn_bwd_workspace_size", "flash_attn_status_string",
                             "flash_attn_last_hip_error", "flash_attn_fwd_blocksparse",
                             "flash_attn_bwd_blocksparse", "flash_attn_decode",
-                            "flash_attn_decode_workspace_size", "flash_attn_fwd_fp8"])
+                            "flash_attn_decode_workspace_size", "flash_attn_fwd_fp8",
+                            "flash_attn_merge"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -241,3 +242,23 @@ def fwd_fp8(**kw):
 ])
 def test_fp8_forward_rejects_bad_arguments(kw, code):
     assert fwd_fp8(**kw) == code
+
+
+def merge(**kw):
+    a = dict(oa=FAKE, la=FAKE, op=FAKE, lp=FAKE, oo=None, rows=64, d=128, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_merge(a["oa"], a["la"], a["op"], a["lp"], a["oo"], a["rows"], a["d"],
+                                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(oa=None), binding.FA_ERR_INVALID_ARG),
+    (dict(lp=None), binding.FA_ERR_INVALID_ARG),
+    (dict(rows=0), binding.FA_ERR_INVALID_ARG),
+    (dict(rows=1 << 25), binding.FA_ERR_INVALID_ARG),   # rows * d >= 2^31
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(op=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+    (dict(oo=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+])
+def test_merge_rejects_bad_arguments(kw, code):
+    assert merge(**kw) == code
