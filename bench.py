@@ -9,7 +9,12 @@ causal.  FLOPs follow the usual convention: forward 4*B*H*N^2*d, halved when
 causal; backward 2.5x the forward (five products, including the recomputed
 Q K^T); softmax work is not counted.
 
-Prints one JSON line (see the design doc for every field).
+Prints one JSON line: the step's throughput and time, the forward and
+backward kernels' figures, the roofline of the dominant kernel (achieved
+against the published peak, with the HBM bytes per launch measured by the
+hardware counters while the kernel sources are unchanged), the CPU oracle's
+throughput on a sample of the same workload, and beside the dense step the
+block-sparse step, the FP8 forward and KV-cache decoding.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -301,8 +306,9 @@ def decode_step(warmup, steps):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): every head is independent and this "
-              "build has no multi-GPU path; see DESIGN.md for how the work would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path. "
+              "Every (batch, head) pair is independent, so across GPUs the work would be split by head.",
+              file=sys.stderr)
         return 2
     import numpy as np
     import torch
