@@ -89,6 +89,16 @@ def measured_traffic(kernel, workload):
     return entry.get("bytes_per_launch") if entry else None
 
 
+def device_info(torch):
+    """The GPU's name, compute units and peak clock, and the dense bf16 MFMA
+    peak they imply (units x clock x 4096 FLOP per cycle on gfx950)."""
+    from io_aware_tiled_attn_amd import binding
+    cus, mhz = binding.flash_attn_device_info(torch.cuda.current_device())
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": cus,
+            "peak_clock_mhz": mhz, "bf16_peak_from_clock_tflops": round(cus * mhz * 1e6 * 4096 / 1e12, 1)}
+
+
 def cpu_baseline(w, inp, gpu_out, heads):
     """Time the float64 oracle on `heads` whole heads of the same workload
     (forward and backward), and compare the GPU results on those heads."""
@@ -426,6 +436,7 @@ def main():
         "kernel_ms": kernel_stats,
         "peak_basis": "MI355X dense bf16 MFMA 2.5 PFLOP/s (published); FLOPs: fwd 4BHN^2d (x1/2 causal), "
                       "bwd 2.5x fwd",
+        "device": device_info(torch),
     }
     if not args.no_blocksparse:
         print("[bench] block-sparse step", file=sys.stderr, flush=True)

@@ -275,6 +275,14 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
 int flash_attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
                      void* o_out, long long rows, int d, void* stream);
 
+/*
+ * Compute units and peak clock (kHz) of HIP device `device`, for reporting
+ * peaks (dense bf16 MFMA: units x clock x 4096 FLOP per cycle on gfx950).
+ * A HIP call; FA_ERR_INVALID_ARG for null outputs or a negative device,
+ * FA_ERR_HIP if the runtime refuses.
+ */
+int flash_attn_device_info(int device, int* cu_count, int* clock_khz);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char* flash_attn_status_string(int status);
 

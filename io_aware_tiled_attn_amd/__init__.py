@@ -20,6 +20,7 @@ __all__ = [
     "flash_attn_decode_workspace_size",
     "flash_attn_bwd_workspace_size",
     "flash_attn_status_string",
+    "flash_attn_device_info",
     "FlashAttnError",
     "library_path",
 ]

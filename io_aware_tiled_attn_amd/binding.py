@@ -76,6 +76,8 @@ def _raw():
     lib.flash_attn_fwd_fp8.restype = i
     lib.flash_attn_merge.argtypes = [vp, vp, vp, vp, vp, ctypes.c_longlong, i, vp]
     lib.flash_attn_merge.restype = i
+    lib.flash_attn_device_info.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.flash_attn_device_info.restype = i
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     lib.flash_attn_last_hip_error.argtypes = []
@@ -195,6 +197,15 @@ def flash_attn_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, s
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd_fp8")
     return out, lse
+
+
+def flash_attn_device_info(device=0):
+    """(compute units, peak clock in MHz) of a HIP device."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    st = _raw().flash_attn_device_info(int(device), ctypes.byref(cus), ctypes.byref(khz))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_device_info")
+    return cus.value, khz.value / 1000.0
 
 
 def flash_attn_merge(o_acc, lse_acc, o_part, lse_part, out=None, stream=None):

@@ -122,6 +122,13 @@ int flash_attn_merge(float* o_acc, float* lse_acc, const void* o_part, const flo
   return hip_status(fa::launch_merge(a));
 }
 
+int flash_attn_device_info(int device, int* cu_count, int* clock_khz) {
+  if (!cu_count || !clock_khz || device < 0) return FA_ERR_INVALID_ARG;
+  hipError_t e = hipDeviceGetAttribute(cu_count, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, device);
+  return hip_status(e);
+}
+
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   if ((long long)B * H * N * d > kMaxElems) return 0;

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
                             "flash_attn_last_hip_error", "flash_attn_fwd_blocksparse",
                             "flash_attn_bwd_blocksparse", "flash_attn_decode",
                             "flash_attn_decode_workspace_size", "flash_attn_fwd_fp8",
-                            "flash_attn_merge"])
+                            "flash_attn_merge", "flash_attn_device_info"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -262,3 +262,10 @@ def merge(**kw):
 ])
 def test_merge_rejects_bad_arguments(kw, code):
     assert merge(**kw) == code
+
+
+def test_device_info_rejects_bad_arguments():
+    x = ctypes.c_int(0)
+    f = binding._raw().flash_attn_device_info
+    assert f(0, None, ctypes.byref(x)) == binding.FA_ERR_INVALID_ARG
+    assert f(-1, ctypes.byref(x), ctypes.byref(x)) == binding.FA_ERR_INVALID_ARG
