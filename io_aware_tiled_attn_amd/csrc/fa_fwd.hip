@@ -52,6 +52,7 @@ constexpr int kSparseBlock = FA_SPARSE_BLOCK;   // block-mask granularity (queri
 #define FWD_LOOKAHEAD 8
 #endif
 
+
 template <int D, int BN>
 struct FwdCfg {
   static constexpr int kWaves = 8;
@@ -200,29 +201,46 @@ __device__ __forceinline__ void softmax_step(const f32x16 (&s)[BN / 32], bf16x8 
 // each one.  Scheduling barriers keep the stream in this order.  voff[dm]
 // is this lane's element offset of its V^T operand reads for feature block
 // dm (swizzled); 16-key steps add 16 D.
+//
+// The operands of the first L products (P V products: V(t) only) are read
+// by matrix_preload.  For d = 128 the kernel issues those reads at the end
+// of the wave's vector phase, before the barrier that opens the matrix
+// phase (V(t) was published a barrier earlier; K(t+1) only by that
+// barrier), so the phase does not open on a full LDS latency.  For d = 64
+// the vector phase is the longer one and the reads stay in the phase.
+template <int D, int BN>
+__device__ __forceinline__ bf16x8 matrix_load(int i, const __bf16* Vs, const int (&voff)[D / 32], const __bf16* Ks,
+                                              const int (&koff)[D / 16]) {
+  constexpr int kPv = BN / 16 * (D / 32);
+  if (i < kPv) {
+    const int c = i / (D / 32), dm = i % (D / 32);
+    return lds_tr_pair(Vs + voff[dm], (16 * c) * D, (16 * c + 8) * D);
+  }
+  const int j = i - kPv, ks = j / (BN / 32), mb = j % (BN / 32);
+  return *(const bf16x8*)(Ks + koff[ks] + 32 * mb * D);
+}
+
 template <int D, int BN, int L>
-__device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16], const __bf16* Vs,
-                                             const int (&voff)[D / 32], f32x16 (&s)[BN / 32], const __bf16* Ks,
-                                             const int (&koff)[D / 16], const bf16x8 (&qb)[D / 16]) {
+__device__ __forceinline__ void matrix_preload(bf16x8 (&ring)[L], const __bf16* Vs, const int (&voff)[D / 32],
+                                               const __bf16* Ks, const int (&koff)[D / 16]) {
+#pragma unroll
+  for (int i = 0; i < L; ++i) ring[i] = matrix_load<D, BN>(i, Vs, voff, Ks, koff);
+}
+
+template <int D, int BN, int L, bool PRELOADED>
+__device__ __forceinline__ void matrix_phase(bf16x8 (&ring)[L], f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16],
+                                             const __bf16* Vs, const int (&voff)[D / 32], f32x16 (&s)[BN / 32],
+                                             const __bf16* Ks, const int (&koff)[D / 16],
+                                             const bf16x8 (&qb)[D / 16]) {
   constexpr int kPv = BN / 16 * (D / 32);   // O += P V products
   constexpr int kS = D / 16 * (BN / 32);    // S = K Q^T products
   constexpr int kAll = kPv + kS;
-  auto load = [&](int i) -> bf16x8 {
-    if (i < kPv) {
-      const int c = i / (D / 32), dm = i % (D / 32);
-      return lds_tr_pair(Vs + voff[dm], (16 * c) * D, (16 * c + 8) * D);
-    }
-    const int j = i - kPv, ks = j / (BN / 32), mb = j % (BN / 32);
-    return *(const bf16x8*)(Ks + koff[ks] + 32 * mb * D);
-  };
 #pragma unroll
   for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
   // The matrix wave takes issue priority over the SIMD's other wave (in its
   // vector phase), so MFMAs are not held back behind its exponentials.
   __builtin_amdgcn_s_setprio(1);
-  bf16x8 ring[L];
-#pragma unroll
-  for (int i = 0; i < L; ++i) ring[i] = load(i);
+  if constexpr (!PRELOADED) matrix_preload<D, BN, L>(ring, Vs, voff, Ks, koff);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kAll; ++i) {
@@ -234,7 +252,7 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&oacc)[D / 32], const bf16x
       const int j = i - kPv, ks = j / (BN / 32), mb = j % (BN / 32);
       s[mb] = mfma32(a, qb[ks], s[mb]);
     }
-    if (i + L < kAll) ring[i % L] = load(i + L);
+    if (i + L < kAll) ring[i % L] = matrix_load<D, BN>(i + L, Vs, voff, Ks, koff);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_setprio(0);
@@ -252,7 +270,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                    const uint8_t* __restrict__ bmask, int N, int BH, int num_qt, float scale_log2) {
   using C = FwdCfg<D, BN>;
-  static_assert(C::BM == 2 * kSparseBlock && kSparseBlock % BN == 0, "sparse blocks vs tiles");
+  static_assert(!SPARSE || (C::BM == 2 * kSparseBlock && kSparseBlock % BN == 0), "sparse blocks vs tiles");
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
   const int tid = threadIdx.x;
@@ -388,6 +406,10 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // buffer's previous tile (t-1) was last read at least one barrier before
   // the copy starts, and the new tile is first read at least one barrier
   // after the wait.
+  constexpr bool kPreload = D == 128;
+  static_assert(!kPreload || FWD_LOOKAHEAD <= BN / 16 * (D / 32), "preloaded products must all be P V products");
+  bf16x8 ring[FWD_LOOKAHEAD];
+  if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(0), voff, kbuf(1), koff);
   if (group == 1) __syncthreads();
 
   int b_cur = 0;   // t % 3
@@ -400,12 +422,13 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // wholly above a wave's queries its P is all zero (the tile is masked
     // like any other), and on the last step the score product reads a stale
     // buffer and its result is not used.
-    matrix_phase<D, BN, FWD_LOOKAHEAD>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
+    matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1).
     if (t + 1 < num_kt) {
       mask_visit(t + 1);
       softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+      if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(b_next), voff, kbuf(b_copy), koff);
     }
     wait_vmem_all();
     __syncthreads();
@@ -556,6 +579,11 @@ hipError_t launch_fwd(const FwdArgs& a) {
     if (a.d == 64) return a.causal ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
     return a.causal ? launch_f32<128, true>(a) : launch_f32<128, false>(a);
   }
+#ifndef FWD_BN128
+#define FWD_BN128 96
+#endif
+  if (a.block_n == 0 && a.d == 128 && a.bmask == nullptr && FWD_BN128 != 64)
+    return a.causal ? launch_bf16<128, FWD_BN128, true, false>(a) : launch_bf16<128, FWD_BN128, false, false>(a);
   const int bn = a.block_n == 0 ? 64 : a.block_n;
   if (a.d == 64) return bn == 32 ? launch_bf16_bn<64, 32>(a) : launch_bf16_bn<64, 64>(a);
   return bn == 32 ? launch_bf16_bn<128, 32>(a) : launch_bf16_bn<128, 64>(a);
