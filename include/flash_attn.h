@@ -86,8 +86,9 @@ int flash_attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Same as flash_attn_fwd with the key-tile width forced: block_n = 0 picks
- * the default, otherwise 32 or 64 keys per tile (bf16 only; the fp32
- * path accepts 0 or 32).  The result must not depend on it (vibeengines.com,
+ * the default (96 keys per tile for bf16 at d = 128 without a block mask,
+ * 64 otherwise), else 32 or 64 keys per tile (bf16 only; the fp32 path
+ * accepts 0 or 32).  The result must not depend on it (vibeengines.com,
  * "Solve it yourself": the block size never changes the answer); tests use
  * it to check that.  Other values return FA_ERR_UNSUPPORTED.
  */
