@@ -74,11 +74,13 @@ def test_forward_small_fp32(N, d, causal):
 def test_block_size_never_changes_answer(d, causal):
     """The pages' assertion that block size does not move the result
     (vibeengines.com, "Solve it yourself"), on the GPU: every key-tile width
-    agrees with the oracle and with the others."""
+    agrees with the oracle and with the others.  block_n = 0 is the default
+    tile: 96 keys for dense d = 128, whose tiles do not divide the 256-query
+    tiles or N = 390."""
     shape = (1, 3, 390, d)
     inp = wl.make_inputs(shape, 3000 + d, "bf16")
     outs = []
-    for bn in (32, 64):
+    for bn in (0, 32, 64):
         announce(f"fwd bf16 shape={shape} causal={causal} block_n={bn}")
         o, lse = run_fwd(inp, "bf16", causal, block_n=bn)
         check_heads(inp, "bf16", causal, o, lse, [(0, h) for h in range(3)])
