@@ -52,7 +52,6 @@ constexpr int kSparseBlock = FA_SPARSE_BLOCK;   // block-mask granularity (queri
 #define FWD_LOOKAHEAD 8
 #endif
 
-
 template <int D, int BN>
 struct FwdCfg {
   static constexpr int kWaves = 8;
@@ -428,6 +427,8 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (t + 1 < num_kt) {
       mask_visit(t + 1);
       softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+      // V(t+1)'s copy was waited for at the end of the previous step, so the
+      // barrier before this phase published it.
       if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(b_next), voff, kbuf(b_copy), koff);
     }
     wait_vmem_all();
