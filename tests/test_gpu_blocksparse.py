@@ -152,3 +152,22 @@ def test_sparse_workload_sampled():
     mask = wl.local_global_block_mask(w.B, w.H, w.N)
     o, lse, grads = run(inp, mask, w.causal)
     check(inp, mask, w.causal, o, lse, grads, [(0, 0), (1, 17), (3, 31)])
+
+
+@pytest.mark.parametrize("pattern", ["stair", "ramp"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse_forward_live_rescale(d, causal, pattern):
+    """Scores that climb across the visited key tiles (tests/rescale_cases.py)
+    under a random block mask: the kernel raises its running max with l and
+    O live (shown on the CPU by tests/test_rescale_model.py for these inputs
+    and this mask)."""
+    from tests import rescale_cases as rc
+    from tests.test_rescale_model import sparse_case_mask
+    N = 520
+    announce(f"block-sparse fwd climbing scores pattern={pattern} d={d} causal={causal}")
+    inp = rc.climbing_bf16((1, 2, N, d), 13, pattern)
+    inp["do"] = np.zeros_like(inp["q"])
+    mask = sparse_case_mask(N)
+    o, lse, _ = run(inp, mask, causal, backward=False)
+    check(inp, mask, causal, o, lse, None, [(0, 0), (0, 1)])

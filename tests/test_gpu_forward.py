@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 from io_aware_tiled_attn_amd import workloads as wl
+from tests import rescale_cases as rc
 from tests.gpu_util import TOL, announce, f64, max_err, to_f64, to_gpu, torch_cuda
 
 pytestmark = pytest.mark.gpu
@@ -196,6 +197,51 @@ def test_forward_is_deterministic():
         o2, l2 = fa().flash_attn_fwd(q, k, v, causal=True)
         torch = torch_cuda()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --------------------------------------------------------------------------
+# The online-softmax update with live state: scores that climb from one key
+# tile to the next, so the running max is raised while l and O already hold
+# mass (vibeengines.com, "The math, worked with real numbers": "Rescale old
+# l", "Absorb new block").  tests/test_rescale_model.py shows on the CPU that
+# these exact inputs make the kernel's rescale branch run for live rows at
+# every tile width used here; "falling" is the control without a raise.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("pattern", rc.PATTERNS)
+@pytest.mark.parametrize("block_n", [0, 32, 64])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_live_rescale(d, causal, block_n, pattern):
+    shape = (1, 2, 520, d)
+    announce(f"fwd bf16 climbing scores pattern={pattern} shape={shape} causal={causal} block_n={block_n}")
+    inp = rc.climbing_bf16(shape, 11, pattern)
+    o, lse = run_fwd(inp, "bf16", causal, block_n=block_n)
+    check_heads(inp, "bf16", causal, o, lse, [(0, 0), (0, 1)])
+
+
+@pytest.mark.parametrize("dtype,d,block_n", [("bf16", 64, 0), ("bf16", 64, 32), ("bf16", 64, 64),
+                                             ("bf16", 128, 0), ("bf16", 128, 32), ("bf16", 128, 64),
+                                             ("fp32", 64, 0), ("fp32", 128, 0)])
+def test_worked_example_across_tiles(dtype, d, block_n):
+    """The page's worked example with its two blocks in different key tiles
+    (keys 0, 1 and 96, 97), scores multiplied by 6 through the scale
+    argument so that the second block's max forces the raise of the running
+    max with the first block's l and O live.  O_0[0:4] are the weights
+    softmax(6 * [2, 1, 3, 0]) in the page's order; LSE_0 = 18 + ln of the
+    sum of e^(6 s - 18)."""
+    q, k, v = rc.worked_across_tiles_f32(d)
+    inp = ({n: wl.f32_to_bf16_bits(a) for n, a in zip("qkv", (q, k, v))} if dtype == "bf16"
+           else dict(zip("qkv", (q, k, v))))
+    announce(f"fwd {dtype} worked example across tiles d={d} block_n={block_n}")
+    o, lse = run_fwd(inp, dtype, False, scale=rc.WORKED_SCALE, block_n=block_n)
+    z = [math.exp(rc.WORKED_SCALE * s - 18.0) for s in rc.WORKED_SCORES]
+    weights = np.array(z) / sum(z)
+    out_round = 2.0 ** -9 if dtype == "bf16" else 1e-6
+    o64 = to_f64(o)
+    np.testing.assert_allclose(o64[0, 0, 0, :4], weights, atol=out_round)
+    assert np.all(o64[0, 0, 0, 4:] == 0.0)
+    assert abs(float(to_f64(lse)[0, 0, 0]) - (18.0 + math.log(sum(z)))) <= 1e-5
+    check_heads(inp, dtype, False, o, lse, [(0, 0)], scale=rc.WORKED_SCALE)
 
 
 # --------------------------------------------------------------------------

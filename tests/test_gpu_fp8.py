@@ -24,6 +24,7 @@ import pytest
 
 import oracle
 from io_aware_tiled_attn_amd import workloads as wl
+from tests import rescale_cases as rc
 from tests.gpu_util import announce, to_f64, torch_cuda
 
 pytestmark = pytest.mark.gpu
@@ -168,3 +169,35 @@ def test_fp8_forward_full_size_sampled():
     rows = np.sort(np.concatenate([[0, 1, 255, 256, w.N - 1], rng.choice(w.N, 59, replace=False)]))
     cases = [(b, h, rows) for b, h in ((0, 0), (1, 7), (2, 19), (3, 31))]
     check(inp, w.causal, o, lse, cases)
+
+
+@pytest.mark.parametrize("pattern", rc.PATTERNS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_forward_live_rescale(d, causal, pattern):
+    """Scores that climb across key tiles (tests/rescale_cases.py): the
+    kernel raises its running max with l and O live (shown on the CPU by
+    tests/test_rescale_model.py for these exact codes); "falling" is the
+    control."""
+    B, H, N = 1, 2, 520
+    announce(f"fp8 forward climbing scores pattern={pattern} d={d} causal={causal}")
+    inp = rc.climbing_fp8((B, H, N, d), 12, pattern)
+    o, lse = run(inp, causal)
+    check(inp, causal, o, lse, all_rows(B, H, N))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_worked_example_across_tiles(d):
+    """The page's worked example in two key tiles with exact E4M3 values
+    (scores 6 * [2, 1, 3, 0] through the scale argument): O_0[0:4] are the
+    weights, LSE_0 = 18 + ln of the sum of e^(6 s - 18)."""
+    import math
+    inp = rc.worked_across_tiles_fp8(d)
+    announce(f"fp8 worked example across tiles d={d}")
+    o, lse = run(inp, False, scale=rc.WORKED_SCALE)
+    z = [math.exp(rc.WORKED_SCALE * s - 18.0) for s in rc.WORKED_SCORES]
+    weights = np.array(z) / sum(z)
+    # E4M3 rounding of P (2^-4 relative) and the bf16 output rounding.
+    np.testing.assert_allclose(o[0, 0, 0, :4], weights, atol=2.0 ** -4 * weights.max() + 2.0 ** -9)
+    assert abs(float(lse[0, 0, 0]) - (18.0 + math.log(sum(z)))) <= 1e-5
+    check(inp, False, o, lse, [(0, 0, np.arange(rc.WORKED_N))], scale=rc.WORKED_SCALE, slope_check=False)
