@@ -33,7 +33,11 @@
  *   - dtype FA_DTYPE_BF16: bfloat16 storage, fp32 accumulation inside the
  *     kernels, round-to-nearest-even on every narrowing.  FA_DTYPE_FP32:
  *     float32 storage and float32 arithmetic throughout (forward only).
- *   - B*H*N*d must stay below 2^31 elements per tensor.
+ *   - B*H*N*d must stay below 2^31 elements per tensor
+ *     (FA_ERR_INVALID_ARG otherwise), and one head's N*d below 2^30
+ *     (FA_ERR_UNSUPPORTED otherwise: inside a head the kernels address
+ *     memory with 32-bit byte offsets, the widest being the backward's fp32
+ *     dQ accumulator of 4*N*d bytes).
  *   - stream is a hipStream_t; NULL means the default stream.  Every call is
  *     asynchronous: it validates its arguments, enqueues kernels on `stream`
  *     and returns.  Faults during execution surface at the caller's next
@@ -215,7 +219,7 @@ int flash_attn_bwd_blocksparse(const void* q, const void* k, const void* v,
  *   o        : [B, H, Nq, d] bf16, written.   lse : [B, H, Nq] fp32 or NULL.
  *   workspace: at least flash_attn_decode_workspace_size(B, H, Nk, d) bytes,
  *              256-byte aligned (per-split partial results), clobbered.
- * bf16 only; d in {64, 128}; B*H*Nk*d below 2^31.  Errors as for
+ * bf16 only; d in {64, 128}; B*H*Nk*d below 2^31 and Nk*d below 2^30.  Errors as for
  * flash_attn_fwd, plus FA_ERR_UNSUPPORTED for Nq > FA_DECODE_MAX_Q and
  * FA_ERR_INVALID_ARG for Nq > Nk or a null or short workspace.
  */

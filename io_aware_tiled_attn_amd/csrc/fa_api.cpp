@@ -23,6 +23,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Largest element count of one [B, H, N, d] tensor the kernels index with
 // 32-bit row arithmetic inside a head and 64-bit offsets across heads.
 constexpr long long kMaxElems = (1LL << 31) - 1;
+// Inside one head the kernels use 32-bit byte offsets and buffer-descriptor
+// sizes; the widest is the backward's fp32 dQ accumulator, 4 N d bytes, so
+// one head's N d must stay below 2^30 (which also keeps a tile read past the
+// head's end, (N + 256) d bf16 elements, inside 32 bits).
+constexpr long long kMaxHeadElems = (1LL << 30) - 1;
 
 int check_sizes(int B, int H, int N, int d, float scale, int causal) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
@@ -30,6 +35,7 @@ int check_sizes(int B, int H, int N, int d, float scale, int causal) {
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if ((long long)B * H * N * d > kMaxElems) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)N * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -191,6 +197,7 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
   if ((long long)B * H * Nk * d > kMaxElems) return FA_ERR_INVALID_ARG;
   if (Nq > Nk) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
   if (Nq > FA_DECODE_MAX_Q) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))

@@ -96,6 +96,16 @@ def test_forward_rejects_bad_arguments(kw, code):
     assert fwd(**kw) == code
 
 
+def test_per_head_size_limit():
+    """N d = 2^30 in one head is refused by every dense entry point (the
+    in-head 32-bit byte offsets); the backward's phases are refused alike."""
+    assert fwd(N=1 << 23, d=128) == binding.FA_ERR_UNSUPPORTED
+    assert fwd(N=1 << 24, d=64, dtype=binding.FA_DTYPE_FP32) == binding.FA_ERR_UNSUPPORTED
+    a = [FAKE] * 9 + [ctypes.c_void_p(0x10000), 1 << 40, 1, 1, 1 << 23, 128, 0.125, 1,
+                      binding.FA_DTYPE_BF16, None, binding.FA_BWD_MAIN]
+    assert binding._raw().flash_attn_bwd_ex(*a) == binding.FA_ERR_UNSUPPORTED
+
+
 def bwd(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
              ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 40, B=1, H=1, N=16, d=64, scale=0.125, causal=1,
@@ -118,6 +128,10 @@ def bwd(**kw):
     (dict(d=32), binding.FA_ERR_UNSUPPORTED),
     (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
     (dict(o=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+    # one head's fp32 dQ accumulator (4 N d bytes) must be addressable with
+    # 32-bit offsets: N d = 2^30 is refused, even though B H N d < 2^31
+    (dict(N=1 << 23, d=128), binding.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, d=64), binding.FA_ERR_UNSUPPORTED),
 ])
 def test_backward_rejects_bad_arguments(kw, code):
     assert bwd(**kw) == code
