@@ -30,6 +30,24 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+
+def host_threads():
+    """Host threads the CPU oracle uses: the cores this process may run on
+    (its affinity mask), capped by an OMP_NUM_THREADS that the host already
+    sets for this process's share of the machine."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
+
+
+# The BLAS thread counts must be in the environment before numpy (or torch,
+# which imports it) is first imported.
+HOST_THREADS = host_threads()
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_var] = str(HOST_THREADS)
+
 METRIC = "attention fwd/bwd TFLOP/s and % of MI355X bf16 MFMA peak at N=4K,d=128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published figure
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published figure
@@ -105,11 +123,14 @@ def cpu_baseline(w, inp, gpu_out, heads):
     import numpy as np
     import oracle
     from io_aware_tiled_attn_amd import workloads as wl
-    try:
+    cores = HOST_THREADS
+    try:   # the BLAS pool numpy actually runs, when threadpoolctl can see it
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            cores = max(pools)
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        pass
     picks = [(b, h) for b in range(w.B) for h in range(w.H)][::max(1, (w.B * w.H) // heads)][:heads]
     errs = {"o": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
     elapsed = 0.0
@@ -139,6 +160,7 @@ def cpu_baseline(w, inp, gpu_out, heads):
         "value": per_head * len(picks) / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{len(picks)} whole heads {picks} of the same workload, forward+backward, float64 numpy "
                   f"({elapsed:.1f} s); FLOPs counted with the GPU's convention (the oracle itself forms the "

@@ -484,7 +484,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     // after the other buffers.
     const int list_bytes = SPARSE ? ((4 * ((a.N + C::BM - 1) / C::BM + 1) + 15) & ~15) : 0;
     const int lds = C::kLdsBytes + list_bytes;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
+      return e;
     const int num_kt = (a.N + C::BN - 1) / C::BN;
     hipLaunchKernelGGL(kern, dim3(num_kt * BH), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta, a.dq_acc,

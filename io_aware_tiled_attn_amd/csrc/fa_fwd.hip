@@ -551,7 +551,8 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   const int lds = C::kLdsBytes + list_bytes;
   // Dynamic LDS above 64 KB must be allowed explicitly; setting the same
   // value from several threads is harmless.
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q,
                      (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, (const uint8_t*)a.bmask, a.N, BH,
                      num_qt, a.scale * kLog2e);

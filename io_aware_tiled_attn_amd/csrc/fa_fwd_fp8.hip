@@ -368,7 +368,9 @@ static hipError_t launch_fp8_d(const FwdFp8Args& a) {
   const int BH = a.B * a.H;
   const int num_qt = (a.N + C::BM - 1) / C::BM;
   auto kern = fa_fwd_fp8_kernel<D, BN, CAUSAL>;
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  const hipError_t e =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), C::kLdsBytes, a.stream, (const uint8_t*)a.q,
                      (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o, a.lse, a.N, BH, num_qt,
                      a.scale * a.q_descale * a.k_descale * kLog2e, a.v_descale);

@@ -33,4 +33,4 @@ from .fp8 import (  # noqa: F401
     attention_forward_fp8_head,
     attention_weights_fp8_head,
 )
-from .online import online_softmax, tiled_attention  # noqa: F401
+from .online import blockwise_softmax, merge_states, tiled_attention  # noqa: F401

@@ -1,12 +1,15 @@
 """GPU parity of block-sparse attention (forward and backward) against the
 float64 oracle with the same block mask, through the C ABI.
 
-Bound: 2e-2 absolute plus 2^-8 of the oracle's magnitude.  A block mask can
-leave a query block with very few keys (here: only the one valid key of a
-ragged last block), and then a gradient is the plain sum of up to 128 dO
-rows, magnitude ~25, whose bf16 rounding alone (half an ulp, 2^-9 relative)
-exceeds any fixed absolute bound; the relative term covers that rounding
-with a factor of 2 for the fp32 and bf16-split arithmetic before it."""
+Bound: 2e-2 absolute, the dense bound, on every element whose oracle value
+is below 8 in magnitude; 2e-2 plus 2^-8 of the oracle's magnitude on the
+elements at or above 8.  A block mask can leave a query block with very few
+keys (here: only the one valid key of a ragged last block), and then a
+gradient is the plain sum of up to 128 dO rows, magnitude ~25, and from 8
+up the bf16 rounding of the output alone (half an ulp: 2^-5 in [8, 16),
+2^-4 in [16, 32)) exceeds 2e-2 whatever the arithmetic; 2^-8 |ref| covers
+that half ulp, the 2e-2 the arithmetic before it.  Each check prints how
+many elements took the wider bound."""
 
 import numpy as np
 import pytest
@@ -40,14 +43,21 @@ def run(inp, mask, causal, backward=True):
     return o, lse, grads
 
 
+WIDE_FROM = 8.0     # |ref| from which half a bf16 ulp (2^-5 at 8) exceeds 2e-2
+WIDE_COUNT = [0]
+
+
 def rel_err(gpu, ref):
-    """max |gpu - ref| - 2^-8 |ref| (0 for an empty array)."""
+    """max of |gpu - ref| - allowance, the allowance being 2^-8 |ref| where
+    |ref| >= 8 and 0 elsewhere (0 for an empty array); compared with 2e-2."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     if gpu.size == 0:
         return 0.0
     assert np.all(np.isfinite(gpu)), "non-finite values in GPU output"
-    return float(np.max(np.abs(gpu - ref) - 2.0 ** -8 * np.abs(ref)))
+    wide = np.abs(ref) >= WIDE_FROM
+    WIDE_COUNT[0] += int(wide.sum())
+    return float(np.max(np.abs(gpu - ref) - np.where(wide, 2.0 ** -8 * np.abs(ref), 0.0)))
 
 
 def check(inp, mask, causal, o, lse, grads, heads):
@@ -68,7 +78,9 @@ def check(inp, mask, causal, o, lse, grads, heads):
             for name, g, r in zip(("dq", "dk", "dv"), g64, ref):
                 worst[name] = max(worst[name], rel_err(g[b, h], r))
             assert np.all(g64[0][b, h][empty] == 0.0)
-    print("  max err (beyond 2^-8 relative) " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()), flush=True)
+    print("  max err (beyond the allowance) " + " ".join(f"{k}={v:.3e}" for k, v in worst.items())
+          + f"; elements at |ref| >= {WIDE_FROM:g}: {WIDE_COUNT[0]}", flush=True)
+    WIDE_COUNT[0] = 0
     for k2, v2 in worst.items():
         assert v2 <= TOL["bf16"], k2
     return worst

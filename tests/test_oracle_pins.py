@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 from oracle import (attention_backward, attention_backward_head,
-                    attention_forward, attention_forward_head, online_softmax,
+                    attention_forward, attention_forward_head, blockwise_softmax,
                     safe_softmax, tiled_attention)
 
 
@@ -108,7 +108,7 @@ def test_worked_example_safe_softmax(golden_dir):
 def test_worked_example_online_trace(golden_dir):
     g = _golden(golden_dir, "worked_example.json")
     half_ulp = 0.5 * 10.0 ** -g["printed_decimals"]
-    w, m, l, trace = online_softmax(g["row"], block=g["block"])
+    w, m, l, trace = blockwise_softmax(g["row"], block=g["block"])
     (m1, l1), (m2, l2) = trace
     assert m1 == g["after_block_1"]["m"]
     assert abs(l1 - g["after_block_1"]["l"]) <= half_ulp
@@ -154,7 +154,7 @@ def test_assertion_online_equals_naive():
         row = list(rng.standard_normal(n) * 3)
         w_naive, m, l = safe_softmax(row)
         for block in (1, 2, 3, n):
-            w_on, m_on, l_on, _ = online_softmax(row, block)
+            w_on, m_on, l_on, _ = blockwise_softmax(row, block)
             np.testing.assert_allclose(w_on, w_naive, atol=1e-15)
             assert m_on == m
             assert abs(l_on - l) < 1e-13
@@ -196,7 +196,7 @@ def test_assertion_valid_distribution():
     rng = np.random.default_rng(13)
     row = list(rng.standard_normal(23) * 5)
     for block in (1, 4, 23):
-        w, _, _, _ = online_softmax(row, block)
+        w, _, _, _ = blockwise_softmax(row, block)
         assert abs(sum(w) - 1.0) < 1e-14
         assert min(w) > 0.0
 
@@ -375,5 +375,5 @@ def test_backward_invariants(causal):
 
 def test_oracle_exports():
     for name in ("attention_forward", "attention_backward", "safe_softmax",
-                 "online_softmax", "tiled_attention", "default_scale"):
+                 "blockwise_softmax", "tiled_attention", "default_scale"):
         assert callable(getattr(oracle, name))
