@@ -169,6 +169,29 @@ int flash_attn_bwd_ex(const void* q, const void* k, const void* v,
                       int phases);
 
 /*
+ * flash_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace lives in a static
+ * device array of FA_BWD_NOALLOC_MAX_BYTES bytes that the library holds on
+ * every GPU it runs on until the process ends; the call allocates nothing
+ * and calls no allocating routine.  Shapes whose workspace
+ * (flash_attn_bwd_workspace_size) exceeds that size return
+ * FA_ERR_UNSUPPORTED; e.g. B*H*N*(d+1) fp32 values up to 16 Mi, as
+ * B4 H16 N2048 d64.  Every call on one GPU uses that GPU's one array, and
+ * each call overwrites it: calls that overlap on one GPU (on different
+ * streams, or from several host threads, without ordering) race and give
+ * wrong gradients; calls ordered on one stream are safe.  Arguments,
+ * results and errors as for flash_attn_bwd (all three kernels run).
+ */
+#define FA_BWD_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d,
+                           float scale, int causal, int dtype, void* stream);
+
+/*
  * Block-sparse attention.  The pages name block-sparse FlashAttention as an
  * approximate extension of the method (chorfi.xyz study guide, "Main
  * concepts to understand"; vibeengines.com lists its Path-256 result among

@@ -13,6 +13,7 @@ __all__ = [
     "flash_attn_fwd_fp8",
     "flash_attn_bwd",
     "flash_attn_bwd_ex",
+    "flash_attn_bwd_noalloc",
     "flash_attn_fwd_blocksparse",
     "flash_attn_bwd_blocksparse",
     "flash_attn_decode",

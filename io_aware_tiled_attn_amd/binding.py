@@ -26,6 +26,7 @@ FA_BWD_ALL = 7
 FA_SPARSE_BLOCK = 128
 FA_SPARSE_MAX_N = 65536
 FA_DECODE_MAX_Q = 16
+FA_BWD_NOALLOC_MAX_BYTES = 64 << 20
 
 _lib = None
 
@@ -64,6 +65,8 @@ def _raw():
     lib.flash_attn_bwd.restype = i
     lib.flash_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp, i]
     lib.flash_attn_bwd_ex.restype = i
+    lib.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd_noalloc.restype = i
     lib.flash_attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.flash_attn_fwd_blocksparse.restype = i
     lib.flash_attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
@@ -399,3 +402,35 @@ def flash_attn_decode(q, k, v, causal=False, scale=None, out=None, lse=None, wor
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_decode")
     return out, lse
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None,
+                           stream=None):
+    """Backward pass whose workspace is the library's static device scratch
+    (FA_BWD_NOALLOC_MAX_BYTES per GPU): the library allocates nothing.
+    Pass dq, dk, dv to keep this wrapper from allocating the outputs with
+    torch.  Calls that overlap on one GPU share the scratch and race; calls
+    on one stream are ordered.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (B, H, N))
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check(t, name, q.dtype, q.shape)
+        outs.append(t)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _raw().flash_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                       lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                       B, H, N, d, float(scale), int(bool(causal)), code, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_noalloc")
+    return tuple(outs)

@@ -159,6 +159,27 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                            dtype, stream, FA_BWD_ALL);
 }
 
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                           int causal, int dtype, void* stream) {
+  // The same checks as flash_attn_bwd (a stand-in workspace pointer passes
+  // the workspace checks), before any HIP call.
+  const void* ws_check = reinterpret_cast<const void*>(uintptr_t{256});
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws_check};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (flash_attn_bwd_workspace_size(B, H, N, d) > FA_BWD_NOALLOC_MAX_BYTES) return FA_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  const hipError_t e = fa::bwd_scratch_address(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, scratch, FA_BWD_NOALLOC_MAX_BYTES, B, H, N, d, scale, causal,
+                  dtype, stream, FA_BWD_ALL, nullptr);
+}
+
 int flash_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                const unsigned char* block_mask, int B, int H, int N, int d, float scale, int causal,
                                int dtype, void* stream) {

@@ -26,10 +26,41 @@
 //      leaves a relative error of up to 2^-9 per element, which at N = 4096
 //      costs up to ~8e-3 absolute in the gradients.
 //   3. bwd_dq_finalize: dQ = scale * accumulator, rounded to bf16.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Device-resident scratch for flash_attn_bwd_noalloc: the backward's
+// workspace (fp32 dQ accumulator and D) for callers that cannot allocate.
+// Every GPU the library runs on holds its own copy from module load until
+// the process ends.  Host code never passes `bwd_scratch` itself to a
+// kernel (on the host that name is a stand-in, not a device address); it
+// uses the per-device address from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char bwd_scratch[FA_BWD_NOALLOC_MAX_BYTES];
+
+hipError_t bwd_scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // First use on this device, with the device current: look up where its
+    // copy of the array lives.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(bwd_scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // 1. D_i = sum_c dO_ic O_ic; zero the dQ accumulator.

@@ -86,6 +86,9 @@ hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_fwd_fp8(const FwdFp8Args& a);
 hipError_t launch_bwd(const BwdArgs& a);
+// This device's address of the static backward scratch
+// (FA_BWD_NOALLOC_MAX_BYTES bytes, 256-byte aligned).
+hipError_t bwd_scratch_address(void** ptr);
 hipError_t launch_decode(const DecodeArgs& a);
 size_t decode_workspace_bytes(int B, int H, int Nk, int d);   // valid sizes only
 float* decode_part_lse(float* part_o, int B, int H, int Nk, int d);   // LSE part of the workspace

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
                             "flash_attn_last_hip_error", "flash_attn_fwd_blocksparse",
                             "flash_attn_bwd_blocksparse", "flash_attn_decode",
                             "flash_attn_decode_workspace_size", "flash_attn_fwd_fp8",
-                            "flash_attn_merge", "flash_attn_device_info"])
+                            "flash_attn_merge", "flash_attn_device_info", "flash_attn_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -283,3 +283,36 @@ def test_device_info_rejects_bad_arguments():
     f = binding._raw().flash_attn_device_info
     assert f(0, None, ctypes.byref(x)) == binding.FA_ERR_INVALID_ARG
     assert f(-1, ctypes.byref(x), ctypes.byref(x)) == binding.FA_ERR_INVALID_ARG
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=1, dtype=binding.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return binding._raw().flash_attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                                 a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                                 a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=None), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=None), binding.FA_ERR_INVALID_ARG),
+    (dict(dv=MISALIGNED), binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=3), binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(dtype=binding.FA_DTYPE_FP32), binding.FA_ERR_UNSUPPORTED),
+    # the workspace of B4 H32 N4096 d128 (270 MB) exceeds the static scratch
+    (dict(B=4, H=32, N=4096, d=128), binding.FA_ERR_UNSUPPORTED),
+])
+def test_noalloc_backward_rejects_bad_arguments(kw, code):
+    assert bwd_noalloc(**kw) == code
+
+
+def test_noalloc_limit_matches_the_workspace_size():
+    """Shapes are accepted exactly while their workspace fits the scratch."""
+    f = binding.flash_attn_bwd_workspace_size
+    assert f(4, 16, 2048, 64) <= binding.FA_BWD_NOALLOC_MAX_BYTES
+    assert f(4, 32, 4096, 128) > binding.FA_BWD_NOALLOC_MAX_BYTES
+    assert f(1, 1, 1 << 17, 128) > binding.FA_BWD_NOALLOC_MAX_BYTES
+    assert bwd_noalloc(N=1 << 17, d=128) == binding.FA_ERR_UNSUPPORTED
