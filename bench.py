@@ -2,12 +2,15 @@
 """Throughput of exact tiled attention on one MI355X: forward + backward.
 
 One step is the whole hot path once: the forward kernel (O and LSE) and the
-three backward kernels (D and dQ-accumulator set-up, the main recompute
-kernel, dQ finalisation) on one batch of seeded synthetic input already
-resident in HBM.  The default workload is B=4, H=32, N=4096, d=128, bf16,
+backward phases (preprocessing: D and the per-head fp16 factors; the
+key-major dK/dV kernel; the query-major dQ kernel) on one batch of seeded
+synthetic input already resident in HBM.  The default workload is B=4, H=32, N=4096, d=128, bf16,
 causal.  FLOPs follow the usual convention: forward 4*B*H*N^2*d, halved when
 causal; backward 2.5x the forward (five products, including the recomputed
-Q K^T); softmax work is not counted.
+Q K^T); softmax work is not counted.  The backward's two main kernels
+execute seven products between them (each recomputes Q K^T and dO V^T):
+the dK/dV kernel four of the five counted ones, the dQ kernel the fifth plus
+the two recomputed ones, which the convention does not count.
 
 Prints one JSON line: the step's throughput and time, the forward and
 backward kernels' figures, the roofline of the dominant kernel (achieved
@@ -82,6 +85,14 @@ def parse_args():
 def flops(w):
     fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
     return fwd, 2.5 * fwd
+
+
+def bwd_kernel_flops(f_bwd):
+    """Counted FLOPs of the dK/dV kernel (S, dP, dV, dK: four of the five
+    products) and of the dQ kernel (dQ), and the dQ kernel's executed FLOPs
+    (S, dP and dQ)."""
+    prod = f_bwd / 5.0
+    return 4.0 * prod, prod, 3.0 * prod
 
 
 def kernel_source_hash():
@@ -224,7 +235,8 @@ def blocksparse_step(q, k, v, do, o, lse, dq, dk, dv, ws, stream, dense_ms, warm
                 "traffic": measured_traffic("fa_fwd_bf16_kernel", w.name)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "main_kernel_traffic": measured_traffic("fa_bwd_main_kernel", w.name)},
+                "dkdv_kernel_traffic": measured_traffic("fa_bwd_dkdv_kernel", w.name),
+                "dq_kernel_traffic": measured_traffic("fa_bwd_dq_kernel", w.name)},
         "tflops": round(tf, 2),
         "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
         "unit": "TFLOP/s on kept blocks",
@@ -407,8 +419,8 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     per_kernel = {name: np.array([e[i].elapsed_time(e[i + 1]) for e in events])
-                  for i, name in enumerate(("forward", "preprocess", "main", "finalize"))}
-    fwd_ms, prep_ms, main_ms, fin_ms = (float(per_kernel[n].mean()) for n in per_kernel)
+                  for i, name in enumerate(("forward", "preprocess", "dkdv", "dq"))}
+    fwd_ms, prep_ms, dkdv_ms, dq_ms = (float(per_kernel[n].mean()) for n in per_kernel)
     kernel_stats = {n: {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
                         "min": round(float(a.min()), 4), "max": round(float(a.max()), 4),
                         "std": round(float(a.std()), 4)} for n, a in per_kernel.items()}
@@ -416,14 +428,13 @@ def main():
     f_fwd, f_bwd = flops(w)
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = f_fwd / (fwd_ms * 1e-3) / 1e12
-    bwd_ms = prep_ms + main_ms + fin_ms
+    bwd_ms = prep_ms + dkdv_ms + dq_ms
     bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
-    main_tf = f_bwd / (main_ms * 1e-3) / 1e12
-    # Dominant kernel of the step: the one with the larger share of time.
-    if main_ms >= fwd_ms:
-        dom, dom_ms, dom_flops = "fa_bwd_main_kernel", main_ms, f_bwd
-    else:
-        dom, dom_ms, dom_flops = "fa_fwd_bf16_kernel", fwd_ms, f_fwd
+    f_dkdv, f_dq, f_dq_exec = bwd_kernel_flops(f_bwd)
+    # Dominant kernel of the step: the one with the largest share of time,
+    # priced at its counted FLOPs.
+    dom, dom_ms, dom_flops = max((("fa_fwd_bf16_kernel", fwd_ms, f_fwd), ("fa_bwd_dkdv_kernel", dkdv_ms, f_dkdv),
+                                  ("fa_bwd_dq_kernel", dq_ms, f_dq)), key=lambda t: t[1])
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic = measured_traffic(dom, w.name)
 
@@ -448,16 +459,17 @@ def main():
                 "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
                 "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                "kernels_ms": {"preprocess": round(prep_ms, 4), "main": round(main_ms, 4),
-                               "finalize": round(fin_ms, 4)},
-                "main_kernel_tflops": round(main_tf, 2)},
+                "kernels_ms": {"preprocess": round(prep_ms, 4), "dkdv": round(dkdv_ms, 4),
+                               "dq": round(dq_ms, 4)},
+                "dkdv_kernel_tflops": round(f_dkdv / (dkdv_ms * 1e-3) / 1e12, 2),
+                "dq_kernel_tflops_executed": round(f_dq_exec / (dq_ms * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "kernel_ms": kernel_stats,
         "peak_basis": "MI355X dense bf16 MFMA 2.5 PFLOP/s (published); FLOPs: fwd 4BHN^2d (x1/2 causal), "
-                      "bwd 2.5x fwd",
+                      "bwd 2.5x fwd (dK/dV kernel 4/5 of it, dQ kernel 1/5 counted, 3/5 executed)",
         "device": device_info(torch),
     }
     if not args.no_blocksparse:

@@ -36,8 +36,8 @@
  *   - B*H*N*d must stay below 2^31 elements per tensor
  *     (FA_ERR_INVALID_ARG otherwise), and one head's N*d below 2^30
  *     (FA_ERR_UNSUPPORTED otherwise: inside a head the kernels address
- *     memory with 32-bit byte offsets, the widest being the backward's fp32
- *     dQ accumulator of 4*N*d bytes).
+ *     memory with 32-bit byte offsets, the widest being a float32 head of
+ *     4*N*d bytes).
  *   - stream is a hipStream_t; NULL means the default stream.  Every call is
  *     asynchronous: it validates its arguments, enqueues kernels on `stream`
  *     and returns.  Faults during execution surface at the caller's next
@@ -103,10 +103,11 @@ int flash_attn_fwd_ex(const void* q, const void* k, const void* v,
                       int block_n);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs: an fp32 dQ accumulator
- * [B, H, N, d] and the fp32 row terms D_i = sum_c dO_ic O_ic [B, H, N],
- * i.e. 4*B*H*N*(d+1) bytes rounded up to 256, linear in N.  Returns 0 for
- * invalid sizes.
+ * Bytes of device workspace flash_attn_bwd needs: the fp32 row terms
+ * D_i = sum_c dO_ic O_ic [B, H, N], the largest |Q|, |dO|, |K|, |V| of
+ * every 256-row chunk (fp32 [B, H, ceil(N/256), 4]) and four fp32 factors
+ * per head, each part rounded up to 256 bytes: about 4*B*H*N*(1 + 1/64)
+ * bytes, linear in N and independent of d.  Returns 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -117,9 +118,14 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d);
  * gradient formulas are the calculus of the forward definition:
  *     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
  *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
- * P and dS enter the dV, dK and dQ products as two bf16 terms each (the
- * rounded value and its residual), so the products see them to 16
- * significant bits; accumulation is fp32.
+ * The products run in fp16 with fp32 accumulation.  Q, dO, K and V enter
+ * them times a power of two per head and tensor that brings the head's
+ * largest magnitude into [1, 2); in fp16 that copy is exact for every value
+ * down to 2^-14 of the largest, so S and dP are exact products of the bf16
+ * inputs, and P and dS enter dV, dK and dQ rounded to fp16 (11 significant
+ * bits).  The factors are divided out in fp32.  Each gradient element is
+ * written once, by one workgroup, in a fixed order: results are
+ * bit-reproducible.
  *   q, k, v, o, dout : [B, H, N, d] bf16, read only (o, lse from the
  *                      forward pass with the same scale and causal flag;
  *                      D is formed from this bf16 o).
@@ -141,13 +147,16 @@ int flash_attn_bwd(const void* q, const void* k, const void* v,
                    float scale, int causal, int dtype, void* stream);
 
 /*
- * flash_attn_bwd split into its three kernels, for callers that time or
- * schedule them separately.  `phases` is a bit mask:
- *   FA_BWD_PREPROCESS (1): D_i = sum_c dO_ic O_ic into the workspace and
- *                          zero the workspace's fp32 dQ accumulator;
- *   FA_BWD_MAIN       (2): recompute P tile by tile, write dK and dV, add
- *                          dQ (unscaled) into the accumulator;
- *   FA_BWD_FINALIZE   (4): dq = scale * accumulator, rounded to bf16.
+ * flash_attn_bwd split into its phases, for callers that time or schedule
+ * them separately.  `phases` is a bit mask:
+ *   FA_BWD_PREPROCESS (1): D_i = sum_c dO_ic O_ic, the chunk maxima and the
+ *                          per-head factors into the workspace (two small
+ *                          kernels);
+ *   FA_BWD_MAIN       (2): one workgroup per 128-key tile recomputes P and
+ *                          dS tile by tile and writes dK and dV;
+ *   FA_BWD_FINALIZE   (4): one workgroup per 128-query tile recomputes P
+ *                          and dS tile by tile and writes dQ.
+ * MAIN and FINALIZE each need PREPROCESS's workspace and not each other.
  * Running the phases in that order, on one stream, with the same arguments
  * and workspace, equals one flash_attn_bwd call (phases = 7).  A mask of 0
  * or with other bits returns FA_ERR_INVALID_ARG.  Other arguments and errors
@@ -176,14 +185,14 @@ int flash_attn_bwd_ex(const void* q, const void* k, const void* v,
  * every GPU it runs on until the process ends; the call allocates nothing
  * and calls no allocating routine.  Shapes whose workspace
  * (flash_attn_bwd_workspace_size) exceeds that size return
- * FA_ERR_UNSUPPORTED; e.g. B*H*N*(d+1) fp32 values up to 16 Mi, as
- * B4 H16 N2048 d64.  Every call on one GPU uses that GPU's one array, and
+ * FA_ERR_UNSUPPORTED; e.g. B*H*N up to about 4.1 Mi rows, as
+ * B4 H32 N16384.  Every call on one GPU uses that GPU's one array, and
  * each call overwrites it: calls that overlap on one GPU (on different
  * streams, or from several host threads, without ordering) race and give
  * wrong gradients; calls ordered on one stream are safe.  Arguments,
  * results and errors as for flash_attn_bwd (all three kernels run).
  */
-#define FA_BWD_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+#define FA_BWD_NOALLOC_MAX_BYTES ((size_t)16 << 20)
 
 int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,

@@ -24,8 +24,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // 32-bit row arithmetic inside a head and 64-bit offsets across heads.
 constexpr long long kMaxElems = (1LL << 31) - 1;
 // Inside one head the kernels use 32-bit byte offsets and buffer-descriptor
-// sizes; the widest is the backward's fp32 dQ accumulator, 4 N d bytes, so
-// one head's N d must stay below 2^30 (which also keeps a tile read past the
+// sizes; the widest is a float32 tensor's head, 4 N d bytes, so one head's
+// N d must stay below 2^30 (which also keeps a tile read past the
 // head's end, (N + 256) d bf16 elements, inside 32 bits).
 constexpr long long kMaxHeadElems = (1LL << 30) - 1;
 
@@ -69,12 +69,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   const size_t need = flash_attn_bwd_workspace_size(B, H, N, d);
   if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
-  const size_t rows = (size_t)B * H * N;
-  const size_t acc_padded = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
-  float* dq_acc = static_cast<float*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_padded);
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dq_acc, delta, B, H, N, d, scale, causal, phases,
-                (hipStream_t)stream, bmask};
+  const fa::BwdWorkspace w = fa::bwd_workspace_layout(B, H, N, d);
+  char* ws = static_cast<char*>(workspace);
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv,
+                reinterpret_cast<float*>(ws + w.delta), reinterpret_cast<float*>(ws + w.part),
+                reinterpret_cast<float*>(ws + w.scales),
+                B, H, N, d, scale, causal, phases, (hipStream_t)stream, bmask};
   return hip_status(fa::launch_bwd(a));
 }
 
@@ -138,11 +138,7 @@ int flash_attn_device_info(int device, int* cu_count, int* clock_khz) {
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   if ((long long)B * H * N * d > kMaxElems) return 0;
-  const size_t rows = (size_t)B * H * N;
-  const size_t acc = rows * (size_t)d * 4;           // fp32 dQ accumulator
-  const size_t acc_padded = (acc + 255) & ~(size_t)255;
-  const size_t bytes = acc_padded + rows * 4;        // fp32 D per row
-  return (bytes + 255) & ~(size_t)255;
+  return fa::bwd_workspace_layout(B, H, N, d).total;
 }
 
 int flash_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -17,6 +17,8 @@
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -29,6 +31,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Both halves of the wave exchange values with the lane 32 away and return
@@ -46,6 +52,12 @@ __device__ __forceinline__ float sum_with_lane_xor32(float x) {
 // fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -89,6 +101,26 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const __bf16* p, int lo, int hi) {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// The same two transposed reads as an fp16 operand.
+__device__ __forceinline__ f16x8 lds_tr_pair_h(const _Float16* p, int lo, int hi) {
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Power-of-two factor 2^e that brings the largest magnitude `amax` of a
+// tensor into [1, 2) (1 when amax is 0 or not finite); e is kept within
+// +-126 so the factor and its inverse are normal fp32 numbers.
+__device__ __forceinline__ float pow2_scale_for(float amax) {
+  if (!(amax > 0.f) || !(amax <= 3.0e38f)) return 1.f;
+  int E;
+  (void)frexpf(amax, &E);   // amax = m 2^E, m in [0.5, 1)
+  const int e = min(126, max(-126, 1 - E));
+  return ldexpf(1.f, e);
 }
 
 // Buffer descriptor over `bytes` bytes at p (raw, 32-bit data format):

@@ -37,6 +37,30 @@ struct FwdFp8Args {
   hipStream_t stream;
 };
 
+// Rows of one head that one preprocessing workgroup covers.
+constexpr int kBwdChunkRows = 256;
+
+// The backward workspace, in this order, each part 256-byte aligned:
+//   delta   fp32 [B, H, N]       D_i = sum_c dO_ic O_ic
+//   part    fp32 [B, H, nch, 4]  largest |Q|, |dO|, |K|, |V| of each 256-row chunk
+//   scales  fp32 [B, H, 4]       per-head power-of-two factors of Q, dO, K, V
+struct BwdWorkspace {
+  size_t delta, part, scales, total;
+};
+inline BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d) {
+  (void)d;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t bh = (size_t)B * H, rows = bh * N;
+  const size_t nch = ((size_t)N + kBwdChunkRows - 1) / kBwdChunkRows;
+  BwdWorkspace w;
+  size_t o = 0;
+  w.delta = o;  o += al(rows * 4);
+  w.part = o;   o += al(bh * nch * 4 * 4);
+  w.scales = o; o += al(bh * 4 * 4);
+  w.total = o;
+  return w;
+}
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -47,8 +71,9 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;   // workspace: fp32 [B, H, N, d]
-  float* delta;    // workspace: fp32 [B, H, N]
+  float* delta;    // workspace parts (bwd_workspace_layout)
+  float* part;
+  float* scales;
   int B, H, N, d;
   float scale;
   int causal;

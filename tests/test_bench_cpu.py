@@ -51,7 +51,7 @@ def test_committed_traffic_file_is_well_formed():
     with open(bench.TRAFFIC_FILE) as f:
         data = json.load(f)
     assert len(data["source_sha"]) == 16 and data["copy_bytes"] > 0
-    assert data["kernels"]["fa_bwd_main_kernel"]["bf16_n4k_d128_causal"]["bytes_per_launch"] > 0
+    assert data["kernels"]["fa_fwd_bf16_kernel"]["bf16_n4k_d128_causal"]["bytes_per_launch"] > 0
     for entries in data["kernels"].values():
         for e in entries.values():
             assert e["bytes_per_launch"] == pytest.approx(e["read_bytes"] + e["write_bytes"], abs=2)

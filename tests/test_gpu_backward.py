@@ -69,11 +69,10 @@ def test_backward_phases_equal_one_call():
         fa().flash_attn_bwd_ex(q, k, v, o, lse, do, causal=True, workspace=ws, dq=outs[0], dk=outs[1],
                                dv=outs[2], phases=ph)
     torch.cuda.synchronize()
-    # dK, dV are written by one workgroup each: identical.  dQ sums float
-    # atomics in arrival order: equal up to fp32 rounding before the bf16 cast.
-    assert torch.equal(outs[1], ref[1]) and torch.equal(outs[2], ref[2])
-    a, b = to_f64(outs[0]), to_f64(ref[0])
-    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(1.0, np.abs(b)))
+    # Every gradient row is written once, by one workgroup, in a fixed
+    # order: identical.
+    for got, want in zip(outs, ref):
+        assert torch.equal(got, want)
 
 
 def test_backward_explicit_scale():

@@ -103,8 +103,7 @@ def test_blocksparse_random_masks(N, d, causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_full_mask_matches_dense_kernels(causal):
     """All pairs kept: the sparse kernels visit every tile the dense kernels
-    visit, in the same order, so O, LSE, dK and dV are bit-identical and dQ
-    (fp32 atomics in another order) agrees to float rounding."""
+    visit, in the same order, so O, LSE, dQ, dK and dV are bit-identical."""
     torch = torch_cuda()
     shape = (2, 2, 384, 64)
     announce(f"blocksparse full mask vs dense shape={shape} causal={causal}")
@@ -117,8 +116,8 @@ def test_full_mask_matches_dense_kernels(causal):
     g2 = fa().flash_attn_bwd_blocksparse(q, k, v, o2, l2, do, ones, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
-    assert max_err(to_f64(g1[0]), to_f64(g2[0])) <= 2 ** -7 * max(1.0, float(g1[0].float().abs().max()))
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 def test_empty_mask_gives_zeros():

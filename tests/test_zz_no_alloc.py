@@ -4,7 +4,6 @@ entry point (flash_attn_bwd, caller-owned workspace) and the oracle, through
 the C ABI: two calls in a row on the same GPU, the second with a smaller
 input, so the second runs on scratch the first left behind."""
 
-import numpy as np
 import pytest
 
 import oracle
@@ -27,11 +26,9 @@ def _case(shape, seed, causal):
     got = fa.flash_attn_bwd_noalloc(q, k, v, o, lse, do, causal=causal, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     assert got[0] is dq and got[1] is dk and got[2] is dv
-    # dK and dV come from the same kernels in the same order: bit-identical;
-    # dQ is summed by float atomics whose order varies: within one bf16 step.
-    assert torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
-    dq64, rq64 = to_f64(dq), to_f64(ref[0])
-    assert max_err(dq64, rq64) <= 2.0 ** -7 * max(1.0, float(np.max(np.abs(rq64))))
+    # The same kernels in the same order, each output written once by one
+    # workgroup: bit-identical.
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
     # and both against the oracle on two heads
     for b, h in ((0, 0), (shape[0] - 1, shape[1] - 1)):
         qh, kh, vh, doh = (f64(inp[n][b, h], "bf16") for n in ("q", "k", "v", "do"))
@@ -52,7 +49,7 @@ def test_noalloc_backward_two_calls_second_smaller(causal):
 def test_noalloc_backward_rejects_a_workspace_beyond_the_scratch():
     torch = torch_cuda()
     import io_aware_tiled_attn_amd as fa
-    shape = (4, 32, 1024, 128)       # 68 MB of workspace
+    shape = (1, 4, 1 << 20, 64)      # 17 MB of workspace
     assert fa.flash_attn_bwd_workspace_size(*shape) > binding.FA_BWD_NOALLOC_MAX_BYTES
     q = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
