@@ -103,11 +103,13 @@ int flash_attn_fwd_ex(const void* q, const void* k, const void* v,
                       int block_n);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs: the fp32 row terms
- * D_i = sum_c dO_ic O_ic [B, H, N], the largest |Q|, |dO|, |K|, |V| of
- * every 256-row chunk (fp32 [B, H, ceil(N/256), 4]) and four fp32 factors
- * per head, each part rounded up to 256 bytes: about 4*B*H*N*(1 + 1/64)
- * bytes, linear in N and independent of d.  Returns 0 for invalid sizes.
+ * Bytes of device workspace flash_attn_bwd needs, each part rounded up to
+ * 256 bytes: D_i = sum_c dO_ic O_ic (fp32 [B, H, N]); the largest |Q|,
+ * |dO|, |K|, |V| of every 256-row chunk (fp32 [B, H, ceil(N/256), 4]); four
+ * fp32 factors per head; two fp32 row terms per row (LSE log2 e and D in the
+ * scaled units); and the scaled fp16 copies of Q, dO, K and V
+ * ([B, H, N, d] each): about B*H*N*(8*d + 12) bytes, linear in N.  Returns
+ * 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -119,8 +121,9 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d);
  *     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
  *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
  * The products run in fp16 with fp32 accumulation.  Q, dO, K and V enter
- * them times a power of two per head and tensor that brings the head's
- * largest magnitude into [1, 2); in fp16 that copy is exact for every value
+ * them as fp16 copies (in the workspace) times a power of two per head and
+ * tensor that brings the head's largest magnitude into [1, 2); that copy is
+ * exact for every value
  * down to 2^-14 of the largest, so S and dP are exact products of the bf16
  * inputs, and P and dS enter dV, dK and dQ rounded to fp16 (11 significant
  * bits).  The factors are divided out in fp32.  Each gradient element is
@@ -149,14 +152,16 @@ int flash_attn_bwd(const void* q, const void* k, const void* v,
 /*
  * flash_attn_bwd split into its phases, for callers that time or schedule
  * them separately.  `phases` is a bit mask:
- *   FA_BWD_PREPROCESS (1): D_i = sum_c dO_ic O_ic, the chunk maxima and the
- *                          per-head factors into the workspace (two small
- *                          kernels);
+ *   FA_BWD_PREPROCESS (1): D_i = sum_c dO_ic O_ic and the chunk maxima,
+ *                          then the per-head factors, the row terms and
+ *                          the scaled fp16 copies of Q and dO, into the
+ *                          workspace (two kernels);
  *   FA_BWD_MAIN       (2): one workgroup per 128-key tile recomputes P and
- *                          dS tile by tile and writes dK and dV;
+ *                          dS tile by tile and writes dK and dV, and the
+ *                          scaled fp16 copies of K and V into the workspace;
  *   FA_BWD_FINALIZE   (4): one workgroup per 128-query tile recomputes P
  *                          and dS tile by tile and writes dQ.
- * MAIN and FINALIZE each need PREPROCESS's workspace and not each other.
+ * Each phase reads what the phases before it wrote to the workspace.
  * Running the phases in that order, on one stream, with the same arguments
  * and workspace, equals one flash_attn_bwd call (phases = 7).  A mask of 0
  * or with other bits returns FA_ERR_INVALID_ARG.  Other arguments and errors
@@ -185,14 +190,14 @@ int flash_attn_bwd_ex(const void* q, const void* k, const void* v,
  * every GPU it runs on until the process ends; the call allocates nothing
  * and calls no allocating routine.  Shapes whose workspace
  * (flash_attn_bwd_workspace_size) exceeds that size return
- * FA_ERR_UNSUPPORTED; e.g. B*H*N up to about 4.1 Mi rows, as
- * B4 H32 N16384.  Every call on one GPU uses that GPU's one array, and
+ * FA_ERR_UNSUPPORTED; e.g. B*H*N*(8*d + 12) bytes up to 64 MiB, as
+ * B2 H16 N2048 d64.  Every call on one GPU uses that GPU's one array, and
  * each call overwrites it: calls that overlap on one GPU (on different
  * streams, or from several host threads, without ordering) race and give
  * wrong gradients; calls ordered on one stream are safe.  Arguments,
  * results and errors as for flash_attn_bwd (all three kernels run).
  */
-#define FA_BWD_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+#define FA_BWD_NOALLOC_MAX_BYTES ((size_t)64 << 20)
 
 int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,

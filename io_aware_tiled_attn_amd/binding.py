@@ -26,7 +26,7 @@ FA_BWD_ALL = 7
 FA_SPARSE_BLOCK = 128
 FA_SPARSE_MAX_N = 65536
 FA_DECODE_MAX_Q = 16
-FA_BWD_NOALLOC_MAX_BYTES = 16 << 20
+FA_BWD_NOALLOC_MAX_BYTES = 64 << 20
 
 _lib = None
 

@@ -73,7 +73,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   char* ws = static_cast<char*>(workspace);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv,
                 reinterpret_cast<float*>(ws + w.delta), reinterpret_cast<float*>(ws + w.part),
-                reinterpret_cast<float*>(ws + w.scales),
+                reinterpret_cast<float*>(ws + w.scales), reinterpret_cast<float*>(ws + w.rowterm),
+                ws + w.q16, ws + w.do16, ws + w.k16, ws + w.v16,
                 B, H, N, d, scale, causal, phases, (hipStream_t)stream, bmask};
   return hip_status(fa::launch_bwd(a));
 }

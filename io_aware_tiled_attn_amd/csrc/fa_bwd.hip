@@ -10,9 +10,8 @@
 //     dQ = scale dS K,         dK = scale dS^T Q.
 //
 // The products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation.
-// Their operands are fp16 copies of Q, dO, K and V, made as the tiles are
-// staged, each scaled by a power of two per head that brings its largest
-// magnitude into [1, 2): a bf16
+// Their operands are fp16 copies of Q, dO, K and V, each scaled by a power
+// of two per head that brings its largest magnitude into [1, 2): a bf16
 // value times a power of two is exact in fp16 down to 2^-14 of that
 // magnitude (fp16 keeps 11 significant bits, bf16 8), so S and dP are the
 // products of the exact inputs, and P (in [0, 1]) and dS (below 2^10 in these
@@ -26,18 +25,15 @@
 // about 40 % of such a pass), two passes each own their output:
 //   1. bwd_prep: per 256-row chunk of a head, D_i = <dO_i, O_i> in fp32 from
 //      the bf16 O, and the chunk's largest |Q|, |dO|, |K|, |V|.
-//   2. bwd_scales: each head's four factors from its chunk maxima.
-//   3. bwd_dkdv: key-major.  One workgroup of 8 waves per 128-key tile: wave
-//      w owns key block w % 4 and the query half w / 4 of every 64-query
-//      step, recomputes S, dP, P and dS for its 32 x 32 block and
-//      accumulates partial dK^T and dV^T; the halves are summed through LDS.
-//   4. bwd_dq: query-major.  One workgroup of 8 waves per 128-query tile:
-//      wave w owns query block w % 4 and the key half w / 4 of every
-//      64-key step, recomputes S^T, dP^T, P^T and dS^T (one query per lane)
-//      and accumulates partial dQ^T; the halves are summed through LDS and
-//      dQ is written once.
+//   2. bwd_convert: the head's factors, the scaled fp16 copies of Q and dO,
+//      and per row LSE log2 e and D in the scaled units.
+//   3. bwd_dkdv: key-major, one workgroup per 128-key tile; writes dK, dV,
+//      and the scaled fp16 copies of its K and V rows.
+//   4. bwd_dq: query-major, one workgroup per 128-query tile; writes dQ.
 // The two passes recompute S and dP each: seven products per (query,
-// key) tile pair instead of five, and no atomics.
+// key) pair instead of five, and no atomics.  The main kernels copy their
+// fp16 tiles global -> LDS with buffer_load ... lds (no registers, no
+// vector instructions), so their vector ALU time goes to P and dS alone.
 #include <mutex>
 
 #include "fa_common.h"
@@ -142,17 +138,152 @@ fa_bwd_prep_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, 
 }
 
 // ---------------------------------------------------------------------------
-// 2. One thread per (head, tensor): the power-of-two factor that brings the
-//    head's largest |Q|, |dO|, |K| or |V| into [1, 2).
+// 2. Per 256-row chunk of a head: the head's factors (from all its chunk
+//    maxima), the chunk's rows of Q and dO times their factors as fp16,
+//    and its row terms (LSE log2 e, +inf for a row that saw no key, so that
+//    P = 0 there; D times the dO and V factors).  The chunk-0 workgroup of
+//    each head records the factors.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ void __launch_bounds__(256)
-fa_bwd_scales_kernel(const float* __restrict__ part, float* __restrict__ scales, int n, int nch) {
-  const int t = blockIdx.x * 256 + threadIdx.x;   // head t / 4, tensor t % 4
-  if (t >= n) return;
-  const float* p = part + (size_t)(t >> 2) * nch * 4 + (t & 3);
-  float m = 0.f;
-  for (int i = 0; i < nch; ++i) m = fmaxf(m, p[4 * i]);
-  scales[t] = pow2_scale_for(m);
+fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+                      const float* __restrict__ delta, const float* __restrict__ part, float* __restrict__ scales,
+                      float* __restrict__ rowterm, _Float16* __restrict__ Q16, _Float16* __restrict__ dO16, int N,
+                      int nch) {
+  __shared__ float red[4];
+  const int bh = blockIdx.x / nch, ch = blockIdx.x % nch;
+  const int tid = threadIdx.x;
+  float f[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float m = 0.f;
+    for (int i = tid; i < nch; i += 256) m = fmaxf(m, part[((size_t)bh * nch + i) * 4 + t]);
+    f[t] = pow2_scale_for(block_max<4>(m, red));
+  }
+  if (ch == 0 && tid == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) scales[bh * 4 + t] = f[t];
+  }
+  const int row0 = ch * kBwdChunkRows;
+  const int rows = min(kBwdChunkRows, N - row0);
+  const size_t rbase = (size_t)bh * N + row0;
+  if (tid < rows) {
+    const float l = LSE[rbase + tid];
+    *(f32x2*)(rowterm + 2 * (rbase + tid)) =
+        (f32x2){l == -INFINITY ? INFINITY : l * kLog2e, delta[rbase + tid] * (f[1] * f[3])};
+  }
+  const __bf16* src[2] = {Q, dO};
+  _Float16* dst[2] = {Q16, dO16};
+  const int n8 = rows * (D / 8);
+  for (int i = tid; i < n8; i += 256) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 x = *(const u32x4*)(src[t] + rbase * D + 8 * (size_t)i);
+      u32x4 y;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) y[w] = pack_f16x2(bf16_lo(x[w]) * f[t], bf16_hi(x[w]) * f[t]);
+      *(u32x4*)(dst[t] + rbase * D + 8 * (size_t)i) = y;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared by the two main kernels: 8 waves in two groups of four (waves 0-3,
+// waves 4-7; one wave of each group per SIMD).  128 rows are resident (keys
+// for dK/dV, queries for dQ); the other side is walked in 32-row blocks, the
+// group g taking blocks g, g + 2, g + 4, ... of the list of visited blocks
+// into two LDS buffers of its own.  A group's step alternates a matrix
+// phase (the gradient products of its previous block and the two
+// score-side products of its current block) and a vector phase (P and dS
+// of the current block, while its next block is copied into LDS); group 1
+// runs one phase behind group 0, so the two waves of a SIMD alternate
+// between the matrix cores and the vector ALU.
+//
+// Tiles sit in LDS as fp16 with unpadded rows whose 16-byte chunks are
+// permuted: chunk c of row r is stored at chunk c ^ f(r).  Both ways a tile
+// is read then hit 64 distinct banks per 256 bytes served:
+//   * rows as MFMA operands (ds_read_b128; 16 lanes = 16 consecutive rows
+//     at one chunk): f is a bijection on the rows of each 16-row group;
+//   * columns with ds_read_b64_tr_b16 (32 lanes = 4 consecutive rows x 4
+//     consecutive chunks, half a chunk each): f puts each of 4 consecutive
+//     rows into a different aligned group of 4 chunks.
+// With t = r / (128 / D) (the rows of one 256-byte bank sweep share t) and
+// L = D / 32: f = 4 (t % L) + (t / L) % 4.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int bwd_swz(int r) {
+  constexpr int kRpb = 128 / D, kL = D / 32;
+  const int t = r / kRpb;
+  return ((t % kL) << 2) | ((t / kL) & 3);
+}
+// Element offset of chunk c (8 fp16 elements) of row r.
+template <int D>
+__device__ __forceinline__ int bwd_chunk_off(int r, int c) {
+  return r * D + 8 * (c ^ bwd_swz<D>(r));
+}
+// The reads below address LDS in bytes from a lane constant and an XOR with
+// a compile-time constant: chunk 2 ks + lg of row r is at byte
+// 2 bwd_chunk_off(r, lg) ^ 32 ks (f only permutes, and 2 ks + lg =
+// 2 ks ^ lg), and the transposing read of rows 16 c + 8 h .. at columns
+// 32 dm .. is at byte (2 bwd_tr_off(lane, 8 h, 0) ^ 64 dm) + 32 c D (the
+// rows' permutation depends on the row only modulo 16, and 32 dm
+// columns are 4 dm chunks, which f's upper bits XOR).  The XOR'd bits are
+// zero in every row's and buffer's base address.
+__device__ __forceinline__ f16x8 lds_row(const _Float16* base, uint32_t byte_off) {
+  return *(const f16x8*)((const char*)base + byte_off);
+}
+__device__ __forceinline__ f16x8 lds_tr_pair_b(const _Float16* base, uint32_t lo_bytes, uint32_t hi_bytes) {
+  return lds_tr_pair_h((const _Float16*)((const char*)base + lo_bytes), 0, (int)(hi_bytes - lo_bytes) / 2);
+}
+// This lane's element offset for the transposing read of rows r0 .. r0 + 3
+// (lanes 0-31; lanes 32-63: rows r0 + 4 .. r0 + 7) at feature columns
+// 32 dm .. 32 dm + 31: lane s = l % 16, G = bit 4, g = bit 5 reads half a
+// chunk of row r0 + 4 g + s / 4 at column 32 dm + 16 G + 4 (s % 4).
+template <int D>
+__device__ __forceinline__ int bwd_tr_off(int lane, int r0, int dm) {
+  const int s = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
+  return bwd_chunk_off<D>(r0 + 4 * g + (s >> 2), 4 * dm + 2 * G + ((s & 3) >> 1)) + 4 * (s & 1);
+}
+
+template <int D>
+struct BwdCfg {
+  static constexpr int kThreads = 512;
+  static constexpr int RES = 128;                  // resident rows per workgroup (4 blocks of 32)
+  static constexpr int BLK = 32;                   // rows of a walked block
+  static constexpr int kResTile = RES * D;         // one resident tensor (dK/dV kernel), fp16 elements
+  static constexpr int kBlkTile = BLK * D;
+  static constexpr int kResBytes = 2 * kResTile * 2;
+  // A staged block: two fp16 tensors, then (dK/dV kernel) the row terms.
+  static constexpr int kStageBytes = 2 * kBlkTile * 2 + BLK * 8;
+  static constexpr int kStagesBytes = 4 * kStageBytes;            // 2 groups x 2 buffers
+  static constexpr int kLdsBytes = kResBytes + kStagesBytes;
+  // Closing sum of the two groups' accumulators: per lane of one group,
+  // the dK/dV kernel's D floats (dK^T and dV^T halves), the dQ kernel's D / 2.
+  static constexpr int kRedBytes = D * 4 * 64 * 4;
+  static constexpr int kLdsTotal = kLdsBytes > kRedBytes ? kLdsBytes : kRedBytes;
+  static constexpr int kDqLdsTotal = kStagesBytes > kRedBytes / 2 ? kStagesBytes : kRedBytes / 2;
+  static_assert(kLdsTotal + 4 * (65536 / BLK + 1) <= 160 * 1024, "LDS budget (with a sparse block list)");
+  static_assert(kResBytes % 1024 == 0 && kStageBytes % 256 == 0 && kBlkTile * 2 % 1024 == 0, "tile alignment");
+};
+
+// Per-head buffer descriptors over the fp16 copies and the row terms: rows
+// past N read as zero.
+struct BwdHead {
+  __amdgpu_buffer_rsrc_t q, k, v, g, rt;
+};
+
+template <int D>
+__device__ __forceinline__ BwdHead bwd_head(const _Float16* Q16, const _Float16* K16, const _Float16* V16,
+                                            const _Float16* dO16, const float* rowterm, int bh, int N) {
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  BwdHead h;
+  h.q = make_rsrc(Q16 + head_off, head_bytes);
+  h.k = make_rsrc(K16 + head_off, head_bytes);
+  h.v = make_rsrc(V16 + head_off, head_bytes);
+  h.g = make_rsrc(dO16 + head_off, head_bytes);
+  h.rt = make_rsrc(rowterm + (size_t)2 * bh * N, (uint32_t)N * 8u);
+  return h;
 }
 
 // bf16 pair times f, rounded to an fp16 pair.
@@ -164,144 +295,241 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float f) {
                  bf16x2_to_f16x2(x[3], f)};
 }
 
-// ---------------------------------------------------------------------------
-// Shared by the two main kernels: 8 waves, 128 rows resident in LDS (keys
-// for dK/dV, queries for dQ) and 64 rows of the other side staged per step
-// through registers into a double-buffered LDS stage.  Rows are padded to
-// D + 8 fp16 elements.
-// ---------------------------------------------------------------------------
-template <int D>
-struct BwdCfg {
-  static constexpr int kThreads = 512;
-  static constexpr int RES = 128;                // resident rows per workgroup (4 blocks of 32)
-  static constexpr int STEP = 64;                // staged rows per step (2 halves of 32)
-  static constexpr int kPitch = D + 8;           // LDS row pitch (fp16 elements)
-  static constexpr int kResTile = RES * kPitch;  // one resident tensor
-  static constexpr int kStepTile = STEP * kPitch;
-  static constexpr int kResBytes = 2 * kResTile * 2;                  // two resident tensors
-  static constexpr int kStageBytes = 2 * kStepTile * 2 + 2 * STEP * 4; // two staged tensors + two row terms
-  static constexpr int kLdsBytes = kResBytes + 2 * kStageBytes;
-  static constexpr int kStageChunks = STEP * D / 8 / kThreads;       // 16-byte chunks per thread and tensor
-  static constexpr int kResChunks = RES * D / 8 / kThreads;
-  // Closing sum of the two halves' accumulators: D floats per lane of four
-  // waves, feature-major.
-  static constexpr int kRedBytes = D * 4 * 64 * 4;
-  static constexpr int kLdsTotal = kLdsBytes > kRedBytes ? kLdsBytes : kRedBytes;
-  // The dQ kernel keeps its resident rows in registers: two stages, or its
-  // closing sum (D / 2 floats per lane of four waves).
-  static constexpr int kDqLdsTotal = 2 * kStageBytes > kRedBytes / 2 ? 2 * kStageBytes : kRedBytes / 2;
-  static_assert(STEP * D / 8 % kThreads == 0 && RES * D / 8 % kThreads == 0, "tile staging");
-  static_assert(kLdsTotal + 4 * (65536 / STEP + 1) <= 160 * 1024, "LDS budget (with a sparse step list)");
-};
-
-// Per-head buffer descriptors: rows past N read as zero.
-struct BwdHead {
-  __amdgpu_buffer_rsrc_t q, k, v, g, lse, dlt;
-};
-
-template <int D>
-__device__ __forceinline__ BwdHead bwd_head(const __bf16* Q, const __bf16* K, const __bf16* V, const __bf16* dO,
-                                            const float* LSE, const float* delta, int bh, int N) {
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  BwdHead h;
-  h.q = make_rsrc(Q + head_off, head_bytes);
-  h.k = make_rsrc(K + head_off, head_bytes);
-  h.v = make_rsrc(V + head_off, head_bytes);
-  h.g = make_rsrc(dO + head_off, head_bytes);
-  h.lse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
-  h.dlt = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4u);
-  return h;
+// Rows row0 .. row0 + ROWS of an fp16 [., D] head into a permuted LDS tile,
+// copied by NW waves (w = 0 .. NW - 1) with buffer_load ... lds: each
+// instruction fills 1 KB of the tile in lane order, lane i fetching the
+// global chunk that the permutation stores at byte 16 i.  Completion is
+// tracked by the issuing wave's vmcnt.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, _Float16* tile, int row0, int w, int lane) {
+  constexpr int kInst = ROWS * D * 2 / 1024;
+  static_assert(kInst % NW == 0, "copy split");
+#pragma unroll
+  for (int i = 0; i < kInst / NW; ++i) {
+    const int inst = w * (kInst / NW) + i;
+    const int byte = inst * 1024 + 16 * lane;
+    const int row = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ bwd_swz<D>(row);
+    lds_copy16(r, (uint32_t)((row0 + row) * D + 8 * c) * 2u, (uint32_t)(uintptr_t)((char*)tile + inst * 1024));
+  }
 }
 
-// Rows r0 .. r0 + ROWS of two bf16 tensors (a, b) into padded fp16 LDS
-// tiles, through registers: load issues the loads, store scales the values
-// by the tensors' factors, rounds them to fp16 and writes them.
-template <int D, int ROWS>
-struct RowPair {
-  static constexpr int kChunks = ROWS * D / 8 / 512;
-  u32x4 a[kChunks], b[kChunks];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int r0, int tid) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * 512;
-      const uint32_t off = (uint32_t)((r0 + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2u;
-      a[i] = bload128(ra, off);
-      b[i] = bload128(rb, off);
+// Wave 0 lists the visited 32-row blocks whose 128-block entry `keep(e)`
+// is nonzero among candidates 0 .. n - 1 into list[1 ..] (count in list[0]),
+// then every wave reads the count.
+template <typename Keep>
+__device__ __forceinline__ int build_block_list(int* list, int n, int wave, int lane, Keep keep) {
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < n; base += 64) {
+      const int e = base + lane;
+      const bool live = e < n && keep(e);
+      const uint64_t bal = __ballot(live);
+      const int pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (live) list[1 + pos] = e;
+      cnt += __popcll(bal);
     }
+    if (lane == 0) list[0] = cnt;
   }
-  __device__ __forceinline__ void store(_Float16* ta, _Float16* tb, float fa, float fb, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * 512;
-      const int off = (c / (D / 8)) * (D + 8) + (c % (D / 8)) * 8;
-      *(u32x4*)(ta + off) = bf16x8_to_f16x8(a[i], fa);
-      *(u32x4*)(tb + off) = bf16x8_to_f16x8(b[i], fb);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(list[0]);
+}
+
+// The matrix phase of a step as one stream of MFMAs whose LDS operands are
+// read kLookahead operands ahead of their product, so the read latency
+// hides behind the preceding products.  The stream is the gradient
+// products of the group's previous block, then the two score-side products
+// of its current block.  Scheduling barriers keep it in this order.  Where
+// a group has no previous or no current block, the stream runs anyway: its
+// P and dS registers then hold zeros (the gradient products add nothing)
+// and the scores it computes from a stale buffer are not used.
+constexpr int kLookahead = 8;
+
+// dK/dV kernel.  Operands: per (c, dm) of the gradient products dO^T then
+// Q^T (transposing reads of the previous block, rows 16 c .. 16 c + 15),
+// then per k-step Q, K, dO, V rows (Q, dO of the current block; K, V
+// resident, already offset to this wave's key block).
+template <int D>
+__device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x16 (&dv_acc)[D / 32],
+                                                  const uint32_t (&pw)[8], const uint32_t (&dsw)[8], f32x16& sc,
+                                                  f32x16& dpc, const _Float16* Qp, const _Float16* Gp,
+                                                  const _Float16* Qc, const _Float16* Gc, const _Float16* Kr,
+                                                  const _Float16* Vr, uint32_t rowx, uint32_t trx0, uint32_t trx1) {
+  constexpr int DM = D / 32, KS = D / 16, L = kLookahead;
+  constexpr int NG = 4 * DM;               // gradient products (one operand read each)
+  constexpr int NS = 2 * KS;               // score products (two operand reads each)
+  constexpr int NL = NG + 2 * NS;          // operand reads
+  auto load = [&](int j) -> f16x8 {
+    if (j < NG) {
+      const int c = (j / 2) / DM, dm = (j / 2) % DM;
+      return lds_tr_pair_b(j % 2 == 0 ? Gp : Qp, (trx0 ^ (64u * dm)) + 32u * c * D, (trx1 ^ (64u * dm)) + 32u * c * D);
     }
+    const int i = j - NG, t = i % 4;
+    const _Float16* base = t == 0 ? Qc : t == 1 ? Kr : t == 2 ? Gc : Vr;
+    return lds_row(base, rowx ^ (32u * (i / 4)));
+  };
+  f16x8 ring[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) ring[j] = load(j);
+  sc = (f32x16){};
+  dpc = (f32x16){};
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  int next = L;   // next operand to read
+#pragma unroll
+  for (int k = 0; k < NG + NS; ++k) {
+    int used;   // operands consumed through this product
+    if (k < NG) {
+      const int c = (k / 2) / DM, dm = (k / 2) % DM;
+      const uint32_t* w = k % 2 == 0 ? pw : dsw;
+      const f16x8 b = __builtin_bit_cast(f16x8, ((u32x4){w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]}));
+      if (k % 2 == 0) dv_acc[dm] = mfma32h(ring[k % L], b, dv_acc[dm]);
+      else dk_acc[dm] = mfma32h(ring[k % L], b, dk_acc[dm]);
+      used = k + 1;
+    } else {
+      const int i = k - NG, j = NG + 4 * (i / 2) + 2 * (i % 2);
+      if (i % 2 == 0) sc = mfma32h(ring[j % L], ring[(j + 1) % L], sc);
+      else dpc = mfma32h(ring[j % L], ring[(j + 1) % L], dpc);
+      used = j + 2;
+    }
+#pragma unroll
+    for (int j = next; j < used + L && j < NL; ++j) ring[j % L] = load(j);
+    next = used + L < NL ? used + L : NL;
+    __builtin_amdgcn_sched_barrier(0);
   }
-};
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// dQ kernel.  Operands: per (c, dm) K^T (transposing read of the previous
+// block), then per k-step K and V rows of the current block; Q and dO are
+// the register B operands.
+template <int D>
+__device__ __forceinline__ void dq_matrix_phase(f32x16 (&dq_acc)[D / 32], const uint32_t (&dsw)[8], f32x16& st,
+                                                f32x16& dpt, const f16x8 (&qbf)[D / 16], const f16x8 (&gbf)[D / 16],
+                                                const _Float16* Kp, const _Float16* Kc, const _Float16* Vc,
+                                                uint32_t rowx, uint32_t trx0, uint32_t trx1) {
+  constexpr int DM = D / 32, KS = D / 16, L = kLookahead;
+  constexpr int NG = 2 * DM;
+  constexpr int NS = 2 * KS;
+  constexpr int NL = NG + NS;              // one operand read per product
+  auto load = [&](int j) -> f16x8 {
+    if (j < NG) {
+      const int c = j / DM, dm = j % DM;
+      return lds_tr_pair_b(Kp, (trx0 ^ (64u * dm)) + 32u * c * D, (trx1 ^ (64u * dm)) + 32u * c * D);
+    }
+    const int i = j - NG;
+    return lds_row(i % 2 == 0 ? Kc : Vc, rowx ^ (32u * (i / 2)));
+  };
+  f16x8 ring[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) ring[j] = load(j);
+  st = (f32x16){};
+  dpt = (f32x16){};
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    if (k < NG) {
+      const int c = k / DM, dm = k % DM;
+      const f16x8 b = __builtin_bit_cast(f16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
+      dq_acc[dm] = mfma32h(ring[k % L], b, dq_acc[dm]);
+    } else {
+      const int i = k - NG;
+      if (i % 2 == 0) st = mfma32h(ring[k % L], qbf[i / 2], st);
+      else dpt = mfma32h(ring[k % L], gbf[i / 2], dpt);
+    }
+    if (k + L < NL) ring[k % L] = load(k + L);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
 
 // ---------------------------------------------------------------------------
-// 3. dK and dV: one workgroup of 8 waves per 128-key tile of one head, two
-//    waves per SIMD.  Wave w owns key block kb = w % 4 (32 keys) and query
-//    half qh = w / 4 of each 64-query step.  K and V of the tile sit in LDS
-//    (their rows are the B operands of S = Q K^T and dP = dO V^T, one key
-//    per lane); Q and dO of the step are staged; dV^T += dO^T P and
-//    dK^T += Q^T dS take their A operands with ds_read_b64_tr_b16.
+// 3. dK and dV: one workgroup per 128-key tile of one head.  Wave w owns key
+//    block kb = w % 4 (32 keys); group g = w / 4 walks every other visited
+//    32-query block.  K and V of the tile sit in LDS (their rows are the B
+//    operands of S = Q K^T and dP = dO V^T, one key per lane); Q and dO of a
+//    block are staged; dV^T += dO^T P and dK^T += Q^T dS take their A
+//    operands with ds_read_b64_tr_b16 and P, dS straight from registers.
 // SPARSE: block-sparse attention.  bmask holds, per head, an nb x nb byte
 // matrix over (128-query block, 128-key block) pairs (a workgroup's keys are
-// one key block); the workgroup visits only the 64-query steps whose query
-// block its mask column keeps, from a list built in LDS.
+// one key block); the workgroup visits only the query blocks its mask
+// column keeps.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(512)
-fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                   const __bf16* __restrict__ dO, const float* __restrict__ LSE,
-                   const float* __restrict__ delta, const float* __restrict__ scales, __bf16* __restrict__ dK,
+fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                   const _Float16* __restrict__ dO16, _Float16* __restrict__ K16, _Float16* __restrict__ V16,
+                   const float* __restrict__ rowterm, const float* __restrict__ scales, __bf16* __restrict__ dK,
                    __bf16* __restrict__ dV, const uint8_t* __restrict__ bmask, int N, int BH, float scale,
                    float scale_log2) {
   using C = BwdCfg<D>;
-  static_assert(C::RES == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::STEP == 0, "sparse blocks vs tiles");
-  constexpr int KS = D / 16;                 // k-steps of the score products
+  static_assert(C::RES == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::BLK == 0, "sparse blocks vs tiles");
   constexpr int DM = D / 32;                 // 32-feature blocks
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  _Float16* Ks = (_Float16*)smem_raw;                              // [RES][kPitch]
+  _Float16* Ks = (_Float16*)smem_raw;                              // [RES][D], permuted chunks
   _Float16* Vs = Ks + C::kResTile;
-  char* stages = smem_raw + C::kResBytes;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // uniform per wave
   const int kb = wave & 3;                   // key block of this wave
-  const int qh = wave >> 2;                  // query half of each step
+  const int g = wave >> 2;                   // group
+  const int gt = tid & 255;                  // thread within the group
   const int lane = tid & 63;
   const int lc = lane & 31, lg = lane >> 5;
-  int kt, bh;   // key tile (small kt = most query steps) and head
+  int kt, bh;   // key tile (small kt = most query blocks) and head
   xcd_head_major(blockIdx.x, BH, (N + C::RES - 1) / C::RES, bh, kt);
-  const BwdHead h = bwd_head<D>(Q, K, V, dO, LSE, delta, bh, N);
+  const BwdHead h = bwd_head<D>(Q16, K16, V16, dO16, rowterm, bh, N);
+  const size_t head_off = (size_t)bh * N * D;
 
   const int k0 = kt * C::RES;                 // first key of the workgroup
   const int kw0 = k0 + kb * 32;               // first key of this wave
   const int key = kw0 + lc;                   // this lane's key column
   const bool key_ok = key < N;
 
-  // In the copies' units: the exponent's multiplier for the scaled S, D's
-  // factor into the scaled dP's units, the epilogue factors of dK and dV.
+  // In the fp16 operands' units: the exponent's multiplier for the scaled
+  // S and the epilogue factors.
   const float sq = scales[bh * 4 + 0], sg = scales[bh * 4 + 1];
   const float sk = scales[bh * 4 + 2], sv = scales[bh * 4 + 3];
   const float c2 = scale_log2 / (sq * sk);
-  const float dsc = sg * sv;
   const float dk_fac = scale / (sg * sv * sq);
   const float dv_fac = 1.f / sg;
 
-  {
-    RowPair<D, C::RES> kv;
-    kv.load(h.k, h.v, k0, tid);
-    kv.store(Ks, Vs, sk, sv, tid);
+  // Visited 32-query blocks: all from jb on (under the causal mask, blocks
+  // before the tile's first key see none of its keys), or those the mask
+  // column keeps; the list sits after the other buffers.
+  const int jb = CAUSAL ? k0 / C::BLK : 0;
+  int n_blk = (N + C::BLK - 1) / C::BLK - jb;
+  int* slist = (int*)(smem_raw + C::kLdsTotal);
+  if constexpr (SPARSE) {
+    const int nb = (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK;
+    const uint8_t* col = bmask + (size_t)bh * nb * nb + kt;   // entry of query block i at col[i * nb]
+    n_blk = build_block_list(slist, n_blk, wave, lane, [&](int e) {
+      return col[(size_t)((jb + e) * C::BLK / FA_SPARSE_BLOCK) * nb] != 0;
+    });
   }
+  auto blk_at = [&](int e) { return jb + (SPARSE ? slist[1 + e] : e); };
+  const int R = (n_blk + 1) / 2;                 // steps of group 0; group 1 has n_blk / 2
+  auto valid = [&](int r) { return 2 * r + g < n_blk; };
 
-  const int qrow_off = (32 * qh + lc) * C::kPitch + 8 * lg;             // Q / dO rows, A operands
-  const int krow_off = (32 * kb + lc) * C::kPitch + 8 * lg;             // K / V rows, B operands
-  const int tr_off = tr_lane_off(lane, C::kPitch, 4) + 32 * qh * C::kPitch;   // Q^T / dO^T
+  char* gstage = smem_raw + C::kResBytes + g * 2 * C::kStageBytes;
+  auto Qb = [&](int b) { return (_Float16*)(gstage + b * C::kStageBytes); };
+  auto Gb = [&](int b) { return Qb(b) + C::kBlkTile; };
+  auto Lb = [&](int b) { return (float*)(Gb(b) + C::kBlkTile); };   // (LSE log2 e, D scaled) per row
+  // The group's step r into buffer b: Q and dO rows and the row terms (rows
+  // past N read as zeros: their Q and dO rows are zero, so they add nothing).
+  auto stage = [&](int r, int b) {
+    const int q0 = blk_at(2 * r + g) * C::BLK;
+    dma_rows<D, C::BLK, 4>(h.q, Qb(b), q0, kb, lane);
+    dma_rows<D, C::BLK, 4>(h.g, Gb(b), q0, kb, lane);
+    if (kb == 0 && lane < C::BLK * 8 / 16)
+      lds_copy16(h.rt, (uint32_t)(q0 * 8 + 16 * lane), (uint32_t)(uintptr_t)Lb(b));
+  };
+
+  // This wave's K / V rows (B operands; row 32 kb + lc has the same chunk
+  // permutation as row lc) and the lane's byte constants of its reads.
+  const int krow_base = 32 * kb * D;
+  const uint32_t rowx = 2u * bwd_chunk_off<D>(lc, lg);
+  const uint32_t trx0 = 2u * bwd_tr_off<D>(lane, 0, 0), trx1 = 2u * bwd_tr_off<D>(lane, 8, 0);
 
   f32x16 dk_acc[DM], dv_acc[DM];
 #pragma unroll
@@ -309,146 +537,117 @@ fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
     dk_acc[i] = (f32x16){};
     dv_acc[i] = (f32x16){};
   }
+  f32x16 sc, dpc;             // S and dP of the current block
+  uint32_t pw[8], dsw[8];     // P and dS of the previous block, fp16 pairs
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pw[i] = dsw[i] = 0u;
 
-  // Query steps (STEP queries each) that can see these keys: all from
-  // qt_begin (dense), or the ones the mask column keeps, listed in LDS after
-  // the other buffers (count first).
-  const int qt_begin = CAUSAL ? k0 / C::STEP : 0;
-  int n_steps = (N + C::STEP - 1) / C::STEP - qt_begin;
-  int* slist = (int*)(smem_raw + C::kLdsTotal);
-  if constexpr (SPARSE) {
-    const int nb = (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK;
-    const uint8_t* col = bmask + (size_t)bh * nb * nb + kt;   // entry of query block i at col[i * nb]
-    if (wave == 0) {
-      int cnt = 0;
-      for (int base = 0; base < n_steps; base += 64) {
-        const int qs = qt_begin + base + lane;
-        const bool live = base + lane < n_steps && col[(size_t)(qs * C::STEP / FA_SPARSE_BLOCK) * nb] != 0;
-        const uint64_t bal = __ballot(live);
-        const int pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        if (live) slist[1 + pos] = qs;
-        cnt += __popcll(bal);
+  // The group's buffers start as zeros (finite operands for the products a
+  // group runs without a block); then the group's first block, and the
+  // resident K, V times their factors as fp16, into LDS and (rows below N)
+  // into the fp16 copies the dQ kernel reads.
+  for (int i = gt; i < 2 * C::kStageBytes / 16; i += 256) ((u32x4*)gstage)[i] = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
+  if (valid(0)) stage(0, 0);
+  {
+    constexpr int kChunks = C::RES * D / 8 / C::kThreads;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_off, (uint32_t)N * D * 2u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_off, (uint32_t)N * D * 2u);
+    u32x4 kx[kChunks], vx[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + i * C::kThreads;
+      const uint32_t off = (uint32_t)((k0 + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2u;
+      kx[i] = bload128(rk, off);
+      vx[i] = bload128(rv, off);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + i * C::kThreads, row = c / (D / 8), ch = c % (D / 8);
+      const u32x4 k16 = bf16x8_to_f16x8(kx[i], sk), v16 = bf16x8_to_f16x8(vx[i], sv);
+      const int lo = bwd_chunk_off<D>(row, ch);
+      *(u32x4*)(Ks + lo) = k16;
+      *(u32x4*)(Vs + lo) = v16;
+      if (k0 + row < N) {
+        const size_t go = head_off + (size_t)(k0 + row) * D + 8 * ch;
+        *(u32x4*)(K16 + go) = k16;
+        *(u32x4*)(V16 + go) = v16;
       }
-      if (lane == 0) slist[0] = cnt;
+    }
+  }
+  wait_vmem_all();
+  __syncthreads();
+  if (g == 1) __syncthreads();
+  for (int r = 0; r <= R; ++r) {
+    // Matrix phase: dV and dK of step r - 1; S and dP of step r.
+    {
+      const int cb = r & 1, pbuf = cb ^ 1;
+      dkdv_matrix_phase<D>(dk_acc, dv_acc, pw, dsw, sc, dpc, Qb(pbuf), Gb(pbuf), Qb(cb), Gb(cb), Ks + krow_base,
+                           Vs + krow_base, rowx, trx0, trx1);
     }
     __syncthreads();
-    n_steps = __builtin_amdgcn_readfirstlane(slist[0]);
-  }
-  auto step_at = [&](int j) { return SPARSE ? slist[1 + j] : qt_begin + j; };
-
-  // Stage: Q and dO rows, LSE * log2 e (+inf past N and for rows that saw
-  // no key, so P = 0 there) and D in the scaled dP's units.
-  RowPair<D, C::STEP> qg;
-  float lse_raw = 0.f, dlt_raw = 0.f;
-  auto load_stage = [&](int q0) {
-    qg.load(h.q, h.g, q0, tid);
-    if (tid < C::STEP) lse_raw = q0 + tid < N ? bload32f(h.lse, (uint32_t)(q0 + tid) * 4u) : INFINITY;
-    else if (tid < 2 * C::STEP) dlt_raw = bload32f(h.dlt, (uint32_t)(q0 + tid - C::STEP) * 4u);
-  };
-  auto store_stage = [&](int buf) {
-    _Float16* Qs = (_Float16*)(stages + buf * C::kStageBytes);
-    _Float16* Gs = Qs + C::kStepTile;
-    float* Ls = (float*)(Gs + C::kStepTile);
-    qg.store(Qs, Gs, sq, sg, tid);
-    if (tid < C::STEP) Ls[tid] = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
-    else if (tid < 2 * C::STEP) Ls[tid] = dlt_raw * dsc;
-  };
-  if (n_steps > 0) {
-    load_stage(step_at(0) * C::STEP);
-    store_stage(0);
-  }
-
-  for (int it = 0; it < n_steps; ++it) {
-    const int q0 = step_at(it) * C::STEP;
-    const bool more = it + 1 < n_steps;
-    if (more) load_stage(step_at(it + 1) * C::STEP);
-    __syncthreads();   // stage `it` (and K, V) visible; the other buffer's last reads done
-    const _Float16* Qs = (const _Float16*)(stages + (it & 1) * C::kStageBytes);
-    const _Float16* Gs = Qs + C::kStepTile;
-    const float* Ls = (const float*)(Gs + C::kStepTile);
-    const float* Ds = Ls + C::STEP;
-    const int qw0 = q0 + 32 * qh;              // first query of this wave's half
-
-    // S = Q K^T and dP = dO V^T, 32 queries x this wave's 32 keys (a wave
-    // whose queries all precede its keys under the causal mask computes a
-    // block of zeros: a branch around it costs more registers than the 2 %
-    // of matrix work it would save).
-    f32x16 sc = (f32x16){}, dpc = (f32x16){};
+    // Vector phase: the copy of step r + 1 into the buffer step r - 1 used
+    // (its last reader was the matrix phase just ended); P = exp2(s c2 -
+    // LSE log2 e) and dS = P (dP - D) of step r as fp16 pairs.
+    if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
+    if (valid(r)) {
+      const int qw0 = blk_at(2 * r + g) * C::BLK;
+      // Keys past N and (causal) keys after the query: P = 0.  The query
+      // offset of register i is 8 (i / 4) + 4 lg + i % 4.
+      if ((kw0 + 31 >= N) || (CAUSAL && qw0 < kw0 + 31)) {
+        const int tl = key_ok ? (CAUSAL ? key - qw0 - 4 * lg : -64) : 64;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 qa = *(const f16x8*)(Qs + qrow_off + 16 * ks);
-      const f16x8 ka = *(const f16x8*)(Ks + krow_off + 16 * ks);
-      const f16x8 ga = *(const f16x8*)(Gs + qrow_off + 16 * ks);
-      const f16x8 va = *(const f16x8*)(Vs + krow_off + 16 * ks);
-      sc = mfma32h(qa, ka, sc);
-      dpc = mfma32h(ga, va, dpc);
-    }
-    // Keys past N and (causal) keys after the query: P = 0.  The query
-    // offset of register r is 8 (r / 4) + 4 lg + r % 4.
-    if ((kw0 + 31 >= N) || (CAUSAL && qw0 < kw0 + 31)) {
-      const int tl = key_ok ? (CAUSAL ? key - qw0 - 4 * lg : -64) : 64;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) >= tl ? sc[r] : -INFINITY;
-    }
-    // P = exp2(s c2 - LSE log2 e), dS = P (dP - D), packed as fp16.
-    uint32_t pw[8], dsw[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 l4 = *(const f32x4*)(Ls + 32 * qh + 8 * i + 4 * lg);
-      const f32x4 d4 = *(const f32x4*)(Ds + 32 * qh + 8 * i + 4 * lg);
-      float p[4], ds[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * i + j;
-        p[j] = fast_exp2(__builtin_fmaf(sc[r], c2, -l4[j]));
-        ds[j] = p[j] * (dpc[r] - d4[j]);
+        for (int i = 0; i < 16; ++i) sc[i] = 8 * (i >> 2) + (i & 3) >= tl ? sc[i] : -INFINITY;
       }
-      pw[2 * i] = pack_f16x2(p[0], p[1]);
-      pw[2 * i + 1] = pack_f16x2(p[2], p[3]);
-      dsw[2 * i] = pack_f16x2(ds[0], ds[1]);
-      dsw[2 * i + 1] = pack_f16x2(ds[2], ds[3]);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS: the A operands read down the
-    // columns in the query order P's accumulator layout leaves in each lane.
+      const float* Ls = Lb(r & 1);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const f16x8 pb = __builtin_bit_cast(f16x8, ((u32x4){pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]}));
-      const f16x8 db = __builtin_bit_cast(f16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
+      for (int i = 0; i < 4; ++i) {
+        // Rows 8 i + 4 lg .. + 3: (LSE log2 e, D) pairs.
+        const f32x4 a4 = *(const f32x4*)(Ls + 2 * (8 * i + 4 * lg));
+        const f32x4 b4 = *(const f32x4*)(Ls + 2 * (8 * i + 4 * lg) + 4);
+        const float l4[4] = {a4[0], a4[2], b4[0], b4[2]}, d4[4] = {a4[1], a4[3], b4[1], b4[3]};
+        float p[4], ds[4];
 #pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-        const int lo = (16 * c) * C::kPitch + 32 * dm, hi = (16 * c + 8) * C::kPitch + 32 * dm;
-        const f16x8 ga = lds_tr_pair_h(Gs + tr_off, lo, hi);
-        const f16x8 qa = lds_tr_pair_h(Qs + tr_off, lo, hi);
-        dv_acc[dm] = mfma32h(ga, pb, dv_acc[dm]);
-        dk_acc[dm] = mfma32h(qa, db, dk_acc[dm]);
+        for (int j = 0; j < 4; ++j) {
+          p[j] = fast_exp2(__builtin_fmaf(sc[4 * i + j], c2, -l4[j]));
+          ds[j] = p[j] * (dpc[4 * i + j] - d4[j]);
+        }
+        pw[2 * i] = pack_f16x2(p[0], p[1]);
+        pw[2 * i + 1] = pack_f16x2(p[2], p[3]);
+        dsw[2 * i] = pack_f16x2(ds[0], ds[1]);
+        dsw[2 * i + 1] = pack_f16x2(ds[2], ds[3]);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pw[i] = dsw[i] = 0u;
     }
-    if (more) store_stage((it + 1) & 1);
+    wait_vmem_all();
+    __syncthreads();
   }
+  if (g == 0) __syncthreads();
 
-  // Sum the two query halves' dK^T and dV^T through LDS (feature-major, so
+  // Sum the two groups' dK^T and dV^T through LDS (feature-major, so
   // consecutive lanes touch consecutive words), then store dK = scale dK^T
   // and dV = dV^T in the inputs' units as bf16 rows of this lane's key.
-  __syncthreads();   // every read of the tile buffers is done
   float* red = (float*)smem_raw;
   auto red_at = [&](int j) { return red + ((size_t)j * 4 + kb) * 64 + lane; };
-  if (qh == 1) {
+  if (g == 1) {
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        *red_at(16 * dm + r) = dk_acc[dm][r];
-        *red_at(D / 2 + 16 * dm + r) = dv_acc[dm][r];
+      for (int i = 0; i < 16; ++i) {
+        *red_at(16 * dm + i) = dk_acc[dm][i];
+        *red_at(D / 2 + 16 * dm + i) = dv_acc[dm][i];
       }
   }
   __syncthreads();
-  if (qh == 0 && key_ok) {
+  if (g == 0 && key_ok) {
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk_acc[dm][r] += *red_at(16 * dm + r);
-        dv_acc[dm][r] += *red_at(D / 2 + 16 * dm + r);
+      for (int i = 0; i < 16; ++i) {
+        dk_acc[dm][i] += *red_at(16 * dm + i);
+        dv_acc[dm][i] += *red_at(D / 2 + 16 * dm + i);
       }
     const size_t row = ((size_t)bh * N + key) * D;
 #pragma unroll
@@ -466,39 +665,39 @@ fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
 }
 
 // ---------------------------------------------------------------------------
-// 4. dQ: one workgroup of 8 waves per 128-query tile of one head.  Wave w
-//    owns query block qb = w % 4 and key half kh = w / 4 of each 64-key
-//    step.  With the scores transposed (S^T = K Q^T, one query per lane),
+// 4. dQ: one workgroup per 128-query tile of one head.  Wave w owns query
+//    block qb = w % 4; group g = w / 4 walks every other visited 32-key
+//    block.  With the scores transposed (S^T = K Q^T, one query per lane),
 //    Q and dO are the B operands (registers), the staged K and V rows the A
 //    operands, and dS^T feeds dQ^T += K^T dS^T straight from registers with
 //    K^T read transposed in the key order the accumulator leaves.
 // SPARSE: the workgroup's 128 queries are one mask row; it visits only the
-// 64-key steps whose key block that row keeps.
+// key blocks that row keeps.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(512)
-fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                 const __bf16* __restrict__ dO, const float* __restrict__ LSE,
-                 const float* __restrict__ delta, const float* __restrict__ scales, __bf16* __restrict__ dQ,
+fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ K16,
+                 const _Float16* __restrict__ V16, const _Float16* __restrict__ dO16,
+                 const float* __restrict__ rowterm, const float* __restrict__ scales, __bf16* __restrict__ dQ,
                  const uint8_t* __restrict__ bmask, int N, int BH, float scale, float scale_log2) {
   using C = BwdCfg<D>;
-  static_assert(C::RES == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::STEP == 0, "sparse blocks vs tiles");
+  static_assert(C::RES == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::BLK == 0, "sparse blocks vs tiles");
   constexpr int KS = D / 16;
   constexpr int DM = D / 32;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  char* stages = smem_raw;   // the resident rows (Q, dO) live in registers here
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = wave & 3;                   // query block of this wave
-  const int kh = wave >> 2;                  // key half of each step
+  const int g = wave >> 2;                   // group
+  const int gt = tid & 255;
   const int lane = tid & 63;
   const int lc = lane & 31, lg = lane >> 5;
   const int num_qt = (N + C::RES - 1) / C::RES;
   int tile, bh;
   xcd_head_major(blockIdx.x, BH, num_qt, bh, tile);
   const int qt = num_qt - 1 - tile;          // heaviest query tiles first (causal)
-  const BwdHead h = bwd_head<D>(Q, K, V, dO, LSE, delta, bh, N);
+  const BwdHead h = bwd_head<D>(Q16, K16, V16, dO16, rowterm, bh, N);
 
   const int qw0 = qt * C::RES + qb * 32;     // first query of this wave
   const int q = qw0 + lc;                    // this lane's query
@@ -507,120 +706,113 @@ fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
   const float c2 = scale_log2 / (sq * sk);
   const float dq_fac = scale / (sk * sg * sv);
 
-  // Q^T and dO^T as B operands: lane holds 8 features of its query's row.
+  // Q^T and dO^T as B operands: lane holds 8 features of its query's row
+  // (zeros past N).
   f16x8 qbf[KS], gbf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint32_t off = (uint32_t)(q * D + 16 * ks + 8 * lg) * 2u;
-    qbf[ks] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(bload128(h.q, off), sq));
-    gbf[ks] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(bload128(h.g, off), sg));
+    qbf[ks] = __builtin_bit_cast(f16x8, bload128(h.q, off));
+    gbf[ks] = __builtin_bit_cast(f16x8, bload128(h.g, off));
   }
-  // This lane's LSE * log2 e (+inf past N or for a row that saw no key, so
-  // P = 0) and D in the scaled dP's units.
+  // This lane's LSE log2 e and D in the scaled dP's units (+inf past N, so
+  // P = 0 there).
   float lq = INFINITY, dq_d = 0.f;
   if (q < N) {
-    const float l = bload32f(h.lse, (uint32_t)q * 4u);
-    lq = l == -INFINITY ? INFINITY : l * kLog2e;
-    dq_d = bload32f(h.dlt, (uint32_t)q * 4u) * (sg * sv);
+    lq = bload32f(h.rt, (uint32_t)q * 8u);
+    dq_d = bload32f(h.rt, (uint32_t)q * 8u + 4u);
   }
 
   f32x16 dq_acc[DM];
 #pragma unroll
   for (int i = 0; i < DM; ++i) dq_acc[i] = (f32x16){};
 
+  // Visited 32-key blocks: all up to the tile's last query (causal) or N,
+  // or those the mask row keeps.
   const int q_tile_end = min(N, (qt + 1) * C::RES);
-  int n_steps = ((CAUSAL ? q_tile_end : N) + C::STEP - 1) / C::STEP;
+  int n_blk = ((CAUSAL ? q_tile_end : N) + C::BLK - 1) / C::BLK;
   int* slist = (int*)(smem_raw + C::kDqLdsTotal);
   if constexpr (SPARSE) {
     const int nb = (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK;
-    const uint8_t* row = bmask + ((size_t)bh * nb + qt) * nb;   // this query block's mask row
-    if (wave == 0) {
-      int cnt = 0;
-      for (int base = 0; base < n_steps; base += 64) {
-        const int ks_ = base + lane;
-        const bool live = ks_ < n_steps && row[ks_ * C::STEP / FA_SPARSE_BLOCK] != 0;
-        const uint64_t bal = __ballot(live);
-        const int pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        if (live) slist[1 + pos] = ks_;
-        cnt += __popcll(bal);
-      }
-      if (lane == 0) slist[0] = cnt;
+    const uint8_t* mrow = bmask + ((size_t)bh * nb + qt) * nb;   // this query block's mask row
+    n_blk = build_block_list(slist, n_blk, wave, lane,
+                             [&](int e) { return mrow[e * C::BLK / FA_SPARSE_BLOCK] != 0; });
+  }
+  auto blk_at = [&](int e) { return SPARSE ? slist[1 + e] : e; };
+  const int R = (n_blk + 1) / 2;
+  auto valid = [&](int r) { return 2 * r + g < n_blk; };
+
+  char* gstage = smem_raw + g * 2 * C::kStageBytes;
+  auto Kb = [&](int b) { return (_Float16*)(gstage + b * C::kStageBytes); };
+  auto Vb = [&](int b) { return Kb(b) + C::kBlkTile; };
+  auto stage = [&](int r, int b) {
+    const int k0 = blk_at(2 * r + g) * C::BLK;
+    dma_rows<D, C::BLK, 4>(h.k, Kb(b), k0, qb, lane);
+    dma_rows<D, C::BLK, 4>(h.v, Vb(b), k0, qb, lane);
+  };
+  const uint32_t rowx = 2u * bwd_chunk_off<D>(lc, lg);
+  const uint32_t trx0 = 2u * bwd_tr_off<D>(lane, 0, 0), trx1 = 2u * bwd_tr_off<D>(lane, 8, 0);
+
+  f32x16 st_acc, dpt;         // S^T and dP^T of the current block
+  uint32_t dsw[8];            // dS^T of the previous block, fp16 pairs
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dsw[i] = 0u;
+
+  // The group's buffers start as zeros (finite operands for the products a
+  // group runs without a block), then take its first block.
+  for (int i = gt; i < 2 * C::kStageBytes / 16; i += 256) ((u32x4*)gstage)[i] = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
+  if (valid(0)) stage(0, 0);
+  wait_vmem_all();
+  __syncthreads();
+  if (g == 1) __syncthreads();
+  for (int r = 0; r <= R; ++r) {
+    // Matrix phase: dQ^T of step r - 1; S^T and dP^T of step r.
+    {
+      const int cb = r & 1, pbuf = cb ^ 1;
+      dq_matrix_phase<D>(dq_acc, dsw, st_acc, dpt, qbf, gbf, Kb(pbuf), Kb(cb), Vb(cb), rowx, trx0, trx1);
     }
     __syncthreads();
-    n_steps = __builtin_amdgcn_readfirstlane(slist[0]);
-  }
-  auto step_at = [&](int j) { return SPARSE ? slist[1 + j] : j; };
-
-  const int krow_off = (32 * kh + lc) * C::kPitch + 8 * lg;                 // K / V rows, A operands
-  const int tr_off = tr_lane_off(lane, C::kPitch, 4) + 32 * kh * C::kPitch;  // K^T, accumulator key order
-
-  RowPair<D, C::STEP> kv;
-  auto stage_k = [&](int buf) { return (_Float16*)(stages + buf * C::kStageBytes); };
-  if (n_steps > 0) {
-    kv.load(h.k, h.v, step_at(0) * C::STEP, tid);
-    kv.store(stage_k(0), stage_k(0) + C::kStepTile, sk, sv, tid);
-  }
-
-  for (int it = 0; it < n_steps; ++it) {
-    const int kst0 = step_at(it) * C::STEP;
-    const bool more = it + 1 < n_steps;
-    if (more) kv.load(h.k, h.v, step_at(it + 1) * C::STEP, tid);
-    __syncthreads();   // stage `it` visible; the other buffer's last reads done
-    const _Float16* Ks = stage_k(it & 1);
-    const _Float16* Vs = Ks + C::kStepTile;
-    const int kw0 = kst0 + 32 * kh;            // first key of this wave's half
-
-    // S^T = K Q^T and dP^T = V dO^T: this wave's 32 keys x 32 queries.
-    f32x16 st = (f32x16){}, dpt = (f32x16){};
+    // Vector phase: the copy of step r + 1 into the buffer step r - 1 used;
+    // P^T = exp2(s c2 - LSE log2 e) and dS^T = P^T (dP^T - D) of step r as
+    // fp16 pairs.
+    if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
+    if (valid(r)) {
+      const int kw0 = blk_at(2 * r + g) * C::BLK;
+      // Keys past N and (causal) keys after the query: P = 0.  The key
+      // offset of register i is 8 (i / 4) + 4 lg + i % 4.
+      if ((kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qw0)) {
+        const int tl = min(N - 1, CAUSAL ? q : N - 1) - kw0 - 4 * lg;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 ka = *(const f16x8*)(Ks + krow_off + 16 * ks);
-      const f16x8 va = *(const f16x8*)(Vs + krow_off + 16 * ks);
-      st = mfma32h(ka, qbf[ks], st);
-      dpt = mfma32h(va, gbf[ks], dpt);
-    }
-    // Keys past N and (causal) keys after the query: P = 0.  The key offset
-    // of register r is 8 (r / 4) + 4 lg + r % 4.
-    if ((kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qw0)) {
-      const int tl = min(N - 1, CAUSAL ? q : N - 1) - kw0 - 4 * lg;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 8 * (r >> 2) + (r & 3) <= tl ? st[r] : -INFINITY;
-    }
-    // P^T = exp2(s c2 - LSE log2 e), dS^T = P^T (dP^T - D), packed as fp16
-    // (the B operands of dQ^T += K^T dS^T).
-    uint32_t dsw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p0 = fast_exp2(__builtin_fmaf(st[2 * i], c2, -lq));
-      const float p1 = fast_exp2(__builtin_fmaf(st[2 * i + 1], c2, -lq));
-      dsw[i] = pack_f16x2(p0 * (dpt[2 * i] - dq_d), p1 * (dpt[2 * i + 1] - dq_d));
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const f16x8 db = __builtin_bit_cast(f16x8, ((u32x4){dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]}));
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-        const int lo = (16 * c) * C::kPitch + 32 * dm, hi = (16 * c + 8) * C::kPitch + 32 * dm;
-        const f16x8 ka = lds_tr_pair_h(Ks + tr_off, lo, hi);
-        dq_acc[dm] = mfma32h(ka, db, dq_acc[dm]);
+        for (int i = 0; i < 16; ++i) st_acc[i] = 8 * (i >> 2) + (i & 3) <= tl ? st_acc[i] : -INFINITY;
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(st_acc[2 * i], c2, -lq));
+        const float p1 = fast_exp2(__builtin_fmaf(st_acc[2 * i + 1], c2, -lq));
+        dsw[i] = pack_f16x2(p0 * (dpt[2 * i] - dq_d), p1 * (dpt[2 * i + 1] - dq_d));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dsw[i] = 0u;
     }
-    if (more) kv.store(stage_k((it + 1) & 1), stage_k((it + 1) & 1) + C::kStepTile, sk, sv, tid);
+    wait_vmem_all();
+    __syncthreads();
   }
+  if (g == 0) __syncthreads();
 
-  // Sum the two key halves' dQ^T through LDS and store dQ = scale dQ^T in
-  // the inputs' units as bf16 rows of this lane's query.
-  __syncthreads();
+  // Sum the two groups' dQ^T through LDS and store dQ = scale dQ^T in the
+  // inputs' units as bf16 rows of this lane's query.
   float* red = (float*)smem_raw;
   auto red_at = [&](int j) { return red + ((size_t)j * 4 + qb) * 64 + lane; };
-  if (kh == 1) {
+  if (g == 1) {
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) *red_at(16 * dm + r) = dq_acc[dm][r];
+      for (int i = 0; i < 16; ++i) *red_at(16 * dm + i) = dq_acc[dm][i];
   }
   __syncthreads();
-  if (kh == 0 && q < N) {
+  if (g == 0 && q < N) {
     const size_t row = ((size_t)bh * N + q) * D;
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
@@ -643,29 +835,34 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   const int BH = a.B * a.H;
   const int nch = (a.N + kBwdChunkRows - 1) / kBwdChunkRows;
   hipError_t e = hipSuccess;
-  // The sparse kernels keep their list of visited steps (count first) after
+  // The sparse kernels keep their list of visited blocks (count first) after
   // the other buffers.
-  const int list_bytes = SPARSE ? ((4 * ((a.N + C::STEP - 1) / C::STEP + 1) + 15) & ~15) : 0;
+  const int list_bytes = SPARSE ? ((4 * ((a.N + C::BLK - 1) / C::BLK + 1) + 15) & ~15) : 0;
   const int lds = C::kLdsTotal + list_bytes;
   const int dq_lds = C::kDqLdsTotal + list_bytes;
   const int num_tiles = (a.N + C::RES - 1) / C::RES;
+  const _Float16* q16 = (const _Float16*)a.q16;
+  const _Float16* k16 = (const _Float16*)a.k16;   // written by the dK/dV kernel
+  const _Float16* v16 = (const _Float16*)a.v16;
+  const _Float16* do16 = (const _Float16*)a.do16;
   if (a.phases & FA_BWD_PREPROCESS) {
     hipLaunchKernelGGL(fa_bwd_prep_kernel<D>, dim3((unsigned)(BH * nch)), dim3(256), 0, a.stream,
                        (const __bf16*)a.o, (const __bf16*)a.dout, (const __bf16*)a.q, (const __bf16*)a.k,
                        (const __bf16*)a.v, a.delta, a.part, a.N, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(fa_bwd_scales_kernel, dim3((unsigned)((4 * BH + 255) / 256)), dim3(256), 0, a.stream,
-                       (const float*)a.part, a.scales, 4 * BH, nch);
+    hipLaunchKernelGGL(fa_bwd_convert_kernel<D>, dim3((unsigned)(BH * nch)), dim3(256), 0, a.stream,
+                       (const __bf16*)a.q, (const __bf16*)a.dout, a.lse, (const float*)a.delta,
+                       (const float*)a.part, a.scales, a.rowterm, (_Float16*)a.q16, (_Float16*)a.do16, a.N, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.phases & FA_BWD_MAIN) {
     auto kern = fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE>;
     if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL(kern, dim3(num_tiles * BH), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta,
-                       a.scales, (__bf16*)a.dk, (__bf16*)a.dv, (const uint8_t*)a.bmask, a.N, BH, a.scale,
-                       a.scale * kLog2e);
+    hipLaunchKernelGGL(kern, dim3(num_tiles * BH), dim3(C::kThreads), lds, a.stream, q16, (const __bf16*)a.k,
+                       (const __bf16*)a.v, do16, (_Float16*)a.k16, (_Float16*)a.v16,
+                       (const float*)a.rowterm, (const float*)a.scales, (__bf16*)a.dk, (__bf16*)a.dv,
+                       (const uint8_t*)a.bmask, a.N, BH, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.phases & FA_BWD_FINALIZE) {
@@ -673,9 +870,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, dq_lds)) !=
         hipSuccess)
       return e;
-    hipLaunchKernelGGL(kern, dim3(num_tiles * BH), dim3(C::kThreads), dq_lds, a.stream, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta,
-                       a.scales, (__bf16*)a.dq, (const uint8_t*)a.bmask, a.N, BH, a.scale, a.scale * kLog2e);
+    hipLaunchKernelGGL(kern, dim3(num_tiles * BH), dim3(C::kThreads), dq_lds, a.stream, q16, k16, v16, do16,
+                       (const float*)a.rowterm, (const float*)a.scales, (__bf16*)a.dq, (const uint8_t*)a.bmask,
+                       a.N, BH, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return e;

@@ -44,19 +44,26 @@ constexpr int kBwdChunkRows = 256;
 //   delta   fp32 [B, H, N]       D_i = sum_c dO_ic O_ic
 //   part    fp32 [B, H, nch, 4]  largest |Q|, |dO|, |K|, |V| of each 256-row chunk
 //   scales  fp32 [B, H, 4]       per-head power-of-two factors of Q, dO, K, V
+//   rowterm fp32 [B, H, N, 2]    per row: LSE log2 e (+inf for a row that saw
+//                                no key) and D times the dO and V factors
+//   q16, do16, k16, v16          fp16 [B, H, N, d] each: the inputs times their factors
 struct BwdWorkspace {
-  size_t delta, part, scales, total;
+  size_t delta, part, scales, rowterm, q16, do16, k16, v16, total;
 };
 inline BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d) {
-  (void)d;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t bh = (size_t)B * H, rows = bh * N;
   const size_t nch = ((size_t)N + kBwdChunkRows - 1) / kBwdChunkRows;
   BwdWorkspace w;
   size_t o = 0;
-  w.delta = o;  o += al(rows * 4);
-  w.part = o;   o += al(bh * nch * 4 * 4);
-  w.scales = o; o += al(bh * 4 * 4);
+  w.delta = o;   o += al(rows * 4);
+  w.part = o;    o += al(bh * nch * 4 * 4);
+  w.scales = o;  o += al(bh * 4 * 4);
+  w.rowterm = o; o += al(rows * 8);
+  w.q16 = o;     o += al(rows * d * 2);
+  w.do16 = o;    o += al(rows * d * 2);
+  w.k16 = o;     o += al(rows * d * 2);
+  w.v16 = o;     o += al(rows * d * 2);
   w.total = o;
   return w;
 }
@@ -74,6 +81,11 @@ struct BwdArgs {
   float* delta;    // workspace parts (bwd_workspace_layout)
   float* part;
   float* scales;
+  float* rowterm;
+  void* q16;
+  void* do16;
+  void* k16;
+  void* v16;
   int B, H, N, d;
   float scale;
   int causal;
