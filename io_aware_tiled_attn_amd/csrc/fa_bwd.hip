@@ -261,7 +261,9 @@ struct BwdCfg {
   // the dK/dV kernel's D floats (dK^T and dV^T halves), the dQ kernel's D / 2.
   static constexpr int kRedBytes = D * 4 * 64 * 4;
   static constexpr int kLdsTotal = kLdsBytes > kRedBytes ? kLdsBytes : kRedBytes;
-  static constexpr int kDqLdsTotal = kStagesBytes > kRedBytes / 2 ? kStagesBytes : kRedBytes / 2;
+  // The dQ kernel's blocks are K and V only, three buffers per group.
+  static constexpr int kDqStageBytes = 2 * kBlkTile * 2;
+  static constexpr int kDqLdsTotal = 6 * kDqStageBytes > kRedBytes / 2 ? 6 * kDqStageBytes : kRedBytes / 2;
   static_assert(kLdsTotal + 4 * (65536 / BLK + 1) <= 160 * 1024, "LDS budget (with a sparse block list)");
   static_assert(kResBytes % 1024 == 0 && kStageBytes % 256 == 0 && kBlkTile * 2 % 1024 == 0, "tile alignment");
 };
@@ -401,12 +403,13 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
 
 // dQ kernel.  Operands: per (c, dm) K^T (transposing read of the previous
 // block), then per k-step K and V rows of the current block; Q and dO are
-// the register B operands.
+// the register B operands.  The score accumulators start at st0 and dpt0
+// (the lane's query's -LSE log2 e / c2 and -D) instead of zero.
 template <int D>
 __device__ __forceinline__ void dq_matrix_phase(f32x16 (&dq_acc)[D / 32], const uint32_t (&dsw)[8], f32x16& st,
                                                 f32x16& dpt, const f16x8 (&qbf)[D / 16], const f16x8 (&gbf)[D / 16],
                                                 const _Float16* Kp, const _Float16* Kc, const _Float16* Vc,
-                                                uint32_t rowx, uint32_t trx0, uint32_t trx1) {
+                                                uint32_t rowx, uint32_t trx0, uint32_t trx1, float st0, float dpt0) {
   constexpr int DM = D / 32, KS = D / 16, L = kLookahead;
   constexpr int NG = 2 * DM;
   constexpr int NS = 2 * KS;
@@ -422,8 +425,14 @@ __device__ __forceinline__ void dq_matrix_phase(f32x16 (&dq_acc)[D / 32], const 
   f16x8 ring[L];
 #pragma unroll
   for (int j = 0; j < L; ++j) ring[j] = load(j);
-  st = (f32x16){};
-  dpt = (f32x16){};
+  // (An empty asm per phase keeps the compiler from holding splatted copies
+  // of the start values across the loop.)
+  asm volatile("" : "+v"(st0), "+v"(dpt0));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    st[i] = st0;
+    dpt[i] = dpt0;
+  }
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -590,12 +599,15 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
     // (its last reader was the matrix phase just ended); P = exp2(s c2 -
     // LSE log2 e) and dS = P (dP - D) of step r as fp16 pairs.
     if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
-    if (valid(r)) {
-      const int qw0 = blk_at(2 * r + g) * C::BLK;
-      // Keys past N and (causal) keys after the query: P = 0.  The query
-      // offset of register i is 8 (i / 4) + 4 lg + i % 4.
-      if ((kw0 + 31 >= N) || (CAUSAL && qw0 < kw0 + 31)) {
-        const int tl = key_ok ? (CAUSAL ? key - qw0 - 4 * lg : -64) : 64;
+    {
+      // A group without a step r masks all its scores (P = dS = 0, so the
+      // next gradient products add nothing).  Otherwise keys past N and
+      // (causal) keys after the query: P = 0.  The query offset of register
+      // i is 8 (i / 4) + 4 lg + i % 4.
+      const bool has = valid(r);
+      const int qw0 = has ? blk_at(2 * r + g) * C::BLK : 0;
+      if (!has || (kw0 + 31 >= N) || (CAUSAL && qw0 < kw0 + 31)) {
+        const int tl = (!has || !key_ok) ? 64 : (CAUSAL ? key - qw0 - 4 * lg : -64);
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 8 * (i >> 2) + (i & 3) >= tl ? sc[i] : -INFINITY;
       }
@@ -617,9 +629,6 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
         dsw[2 * i] = pack_f16x2(ds[0], ds[1]);
         dsw[2 * i + 1] = pack_f16x2(ds[2], ds[3]);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pw[i] = dsw[i] = 0u;
     }
     wait_vmem_all();
     __syncthreads();
@@ -715,12 +724,13 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
     qbf[ks] = __builtin_bit_cast(f16x8, bload128(h.q, off));
     gbf[ks] = __builtin_bit_cast(f16x8, bload128(h.g, off));
   }
-  // This lane's LSE log2 e and D in the scaled dP's units (+inf past N, so
-  // P = 0 there).
-  float lq = INFINITY, dq_d = 0.f;
+  // Start values of this lane's S^T and dP^T accumulators: -LSE log2 e / c2
+  // (-inf past N, so P = 0 there) and -D in the scaled dP's units; then
+  // P^T = exp2(c2 S^T) and dS^T = P^T dP^T.
+  float st0 = -INFINITY, dpt0 = 0.f;
   if (q < N) {
-    lq = bload32f(h.rt, (uint32_t)q * 8u);
-    dq_d = bload32f(h.rt, (uint32_t)q * 8u + 4u);
+    st0 = -bload32f(h.rt, (uint32_t)q * 8u) / c2;
+    dpt0 = -bload32f(h.rt, (uint32_t)q * 8u + 4u);
   }
 
   f32x16 dq_acc[DM];
@@ -742,9 +752,11 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
   const int R = (n_blk + 1) / 2;
   auto valid = [&](int r) { return 2 * r + g < n_blk; };
 
-  char* gstage = smem_raw + g * 2 * C::kStageBytes;
-  auto Kb = [&](int b) { return (_Float16*)(gstage + b * C::kStageBytes); };
+  // Three buffers per group: step r in buffer r % 3, copied two steps ahead.
+  char* gstage = smem_raw + g * 3 * C::kDqStageBytes;
+  auto Kb = [&](int b) { return (_Float16*)(gstage + b * C::kDqStageBytes); };
   auto Vb = [&](int b) { return Kb(b) + C::kBlkTile; };
+  constexpr int kCopies = 2 * (C::BLK * D * 2 / 1024) / 4;   // copy instructions per wave and step
   auto stage = [&](int r, int b) {
     const int k0 = blk_at(2 * r + g) * C::BLK;
     dma_rows<D, C::BLK, 4>(h.k, Kb(b), k0, qb, lane);
@@ -759,45 +771,49 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
   for (int i = 0; i < 8; ++i) dsw[i] = 0u;
 
   // The group's buffers start as zeros (finite operands for the products a
-  // group runs without a block), then take its first block.
-  for (int i = gt; i < 2 * C::kStageBytes / 16; i += 256) ((u32x4*)gstage)[i] = (u32x4){0u, 0u, 0u, 0u};
+  // group runs without a block), then take its first two blocks.
+  for (int i = gt; i < 3 * C::kDqStageBytes / 16; i += 256) ((u32x4*)gstage)[i] = (u32x4){0u, 0u, 0u, 0u};
   __syncthreads();
   if (valid(0)) stage(0, 0);
+  if (valid(1)) stage(1, 1);
   wait_vmem_all();
   __syncthreads();
   if (g == 1) __syncthreads();
+  int cb = 0;   // r % 3
   for (int r = 0; r <= R; ++r) {
+    const int pbuf = cb == 0 ? 2 : cb - 1, nbuf = cb == 2 ? 0 : cb + 1;   // (r - 1) % 3, (r + 1) % 3
     // Matrix phase: dQ^T of step r - 1; S^T and dP^T of step r.
-    {
-      const int cb = r & 1, pbuf = cb ^ 1;
-      dq_matrix_phase<D>(dq_acc, dsw, st_acc, dpt, qbf, gbf, Kb(pbuf), Kb(cb), Vb(cb), rowx, trx0, trx1);
-    }
+    dq_matrix_phase<D>(dq_acc, dsw, st_acc, dpt, qbf, gbf, Kb(pbuf), Kb(cb), Vb(cb), rowx, trx0, trx1, st0, dpt0);
     __syncthreads();
-    // Vector phase: the copy of step r + 1 into the buffer step r - 1 used;
-    // P^T = exp2(s c2 - LSE log2 e) and dS^T = P^T (dP^T - D) of step r as
-    // fp16 pairs.
-    if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
-    if (valid(r)) {
-      const int kw0 = blk_at(2 * r + g) * C::BLK;
-      // Keys past N and (causal) keys after the query: P = 0.  The key
-      // offset of register i is 8 (i / 4) + 4 lg + i % 4.
-      if ((kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qw0)) {
-        const int tl = min(N - 1, CAUSAL ? q : N - 1) - kw0 - 4 * lg;
+    // Vector phase: the copy of step r + 2 into the buffer step r - 1 used
+    // (its last reader was the matrix phase just ended); P^T = exp2(c2 S^T)
+    // and dS^T = P^T dP^T of step r as fp16 pairs.
+    const bool copy = valid(r + 2);
+    if (copy) stage(r + 2, pbuf);
+    {
+      // A group without a step r masks all its scores (P = dS = 0).
+      // Otherwise keys past N and (causal) keys after the query: P = 0.
+      // The key offset of register i is 8 (i / 4) + 4 lg + i % 4.
+      const bool has = valid(r);
+      const int kw0 = has ? blk_at(2 * r + g) * C::BLK : 0;
+      if (!has || (kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qw0)) {
+        const int tl = has ? min(N - 1, CAUSAL ? q : N - 1) - kw0 - 4 * lg : -64;
 #pragma unroll
         for (int i = 0; i < 16; ++i) st_acc[i] = 8 * (i >> 2) + (i & 3) <= tl ? st_acc[i] : -INFINITY;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(__builtin_fmaf(st_acc[2 * i], c2, -lq));
-        const float p1 = fast_exp2(__builtin_fmaf(st_acc[2 * i + 1], c2, -lq));
-        dsw[i] = pack_f16x2(p0 * (dpt[2 * i] - dq_d), p1 * (dpt[2 * i + 1] - dq_d));
+        const float p0 = fast_exp2(st_acc[2 * i] * c2);
+        const float p1 = fast_exp2(st_acc[2 * i + 1] * c2);
+        dsw[i] = pack_f16x2(p0 * dpt[2 * i], p1 * dpt[2 * i + 1]);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dsw[i] = 0u;
     }
-    wait_vmem_all();
+    // Step r + 1's copy (issued a step ago) has landed; step r + 2's may
+    // still be in flight (this loop issues no other memory loads).
+    if (copy) wait_vmem_keep<kCopies>();
+    else wait_vmem_all();
     __syncthreads();
+    cb = nbuf;
   }
   if (g == 0) __syncthreads();
 
@@ -839,7 +855,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   // the other buffers.
   const int list_bytes = SPARSE ? ((4 * ((a.N + C::BLK - 1) / C::BLK + 1) + 15) & ~15) : 0;
   const int lds = C::kLdsTotal + list_bytes;
-  const int dq_lds = C::kDqLdsTotal + list_bytes;
+  const int dq_lds = C::kDqLdsTotal + list_bytes;   // the list sits after the buffers
   const int num_tiles = (a.N + C::RES - 1) / C::RES;
   const _Float16* q16 = (const _Float16*)a.q16;
   const _Float16* k16 = (const _Float16*)a.k16;   // written by the dK/dV kernel

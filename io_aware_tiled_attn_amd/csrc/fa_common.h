@@ -156,6 +156,13 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t go
 
 // s_waitcnt vmcnt(0), leaving the other counters alone.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but the N most recent vector memory loads have
+// completed (they complete in issue order); the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Work order for a launch of num_tiles x BH workgroups (tile-major work
 // items of BH heads).  The dispatcher hands workgroup i to XCD i % 8, and
