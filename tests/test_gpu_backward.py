@@ -77,15 +77,27 @@ def test_backward_phases_equal_one_call():
 
 def test_backward_explicit_scale():
     """A non-default scale must reach every product (a scale applied twice
-    or not at all moves the gradients far beyond the bound).  With much
-    sharper attention (scale 0.2 at d = 64) the largest dK of this input
-    reaches 4.46, where the bf16 spacing is 0.031; output rounding then takes
-    most of the 2e-2 budget, so the test uses 0.1."""
+    or not at all moves the gradients far beyond the bound); 0.1 at d = 64
+    is softer than the default 1/8 (test_backward_sharp_scale takes 0.2)."""
     shape = (1, 2, 260, 64)
     inp = wl.make_inputs(shape, 4100, "bf16", with_grad=True)
     announce(f"bwd shape={shape} scale=0.1")
     grads = run_fwd_bwd(inp, True, scale=0.1)
     check_grads(inp, True, grads, [(0, 0), (0, 1)], scale=0.1)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_sharp_scale(causal):
+    """Sharper attention, scale 0.2 at d = 64 (1.6x the default 1/8): the
+    largest dK of this input is about 4.5, where half a bf16 step is 0.016,
+    so the output rounding alone takes most of the 2e-2 bound and the
+    arithmetic before it (fp16 P and dS, D from the bf16 O) must stay
+    within the rest."""
+    shape = (1, 2, 260, 64)
+    inp = wl.make_inputs(shape, 4100, "bf16", with_grad=True)
+    announce(f"bwd shape={shape} scale=0.2 causal={causal}")
+    grads = run_fwd_bwd(inp, causal, scale=0.2)
+    check_grads(inp, causal, grads, [(0, 0), (0, 1)], scale=0.2)
 
 
 def _invariants(inp, grads, causal):
