@@ -38,6 +38,7 @@
 
 #include "fa_common.h"
 #include "fa_internal.h"
+#include "fa_layout.h"
 
 namespace fa {
 
@@ -210,17 +211,10 @@ fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ d
 // With t = r / (128 / D) (the rows of one 256-byte bank sweep share t) and
 // L = D / 32: f = 4 (t % L) + (t / L) % 4.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int bwd_swz(int r) {
-  constexpr int kRpb = 128 / D, kL = D / 32;
-  const int t = r / kRpb;
-  return ((t % kL) << 2) | ((t / kL) & 3);
-}
-// Element offset of chunk c (8 fp16 elements) of row r.
-template <int D>
-__device__ __forceinline__ int bwd_chunk_off(int r, int c) {
-  return r * D + 8 * (c ^ bwd_swz<D>(r));
-}
+using layout::bwd_chunk_off;
+using layout::bwd_swz;
+using layout::bwd_tr_off;
+
 // The reads below address LDS in bytes from a lane constant and an XOR with
 // a compile-time constant: chunk 2 ks + lg of row r is at byte
 // 2 bwd_chunk_off(r, lg) ^ 32 ks (f only permutes, and 2 ks + lg =
@@ -309,8 +303,8 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, _Float16* til
 #pragma unroll
   for (int i = 0; i < kInst / NW; ++i) {
     const int inst = w * (kInst / NW) + i;
-    const int byte = inst * 1024 + 16 * lane;
-    const int row = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ bwd_swz<D>(row);
+    int row, c;
+    layout::copy_slot(2 * D, inst, lane, bwd_swz<D>, row, c);
     lds_copy16(r, (uint32_t)((row0 + row) * D + 8 * c) * 2u, (uint32_t)(uintptr_t)((char*)tile + inst * 1024));
   }
 }

@@ -43,6 +43,7 @@
 //     per XCD, even though the latter reads K and V from memory only once.
 #include "fa_common.h"
 #include "fa_internal.h"
+#include "fa_layout.h"
 
 namespace fa {
 
@@ -68,22 +69,12 @@ struct FwdCfg {
   static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
 };
 
-// Tiles sit in LDS with unpadded rows; the 16-byte chunks of each row are
-// permuted (chunk c of row r is stored at chunk c ^ f(r)) so that the reads
-// of both products hit 64 distinct banks:
-//   * K, read as MFMA A operands (16 lanes = 16 consecutive rows at one
-//     chunk): f spreads 16 consecutive rows over all chunk positions.
-//   * V, read with ds_read_b64_tr_b16 (a half-wave covers 4 consecutive
-//     rows x 4 consecutive chunks): f moves each of 4 consecutive rows to
-//     a different group of 4 chunks.
-// Rows per 256-byte bank sweep: 1 for d = 128, 2 for d = 64.
+// Tiles sit in LDS with unpadded rows whose 16-byte chunks are permuted
+// (layout::FwdSwizzle: K by its row-read permutation, V by its
+// transposing-read permutation), so that the reads of both products hit 64
+// distinct banks.
 template <int D>
-struct Swizzle {
-  static constexpr int kCpr = D / 8;     // chunks per row
-  static constexpr int kRpb = 128 / D;   // rows per bank sweep
-  __device__ static int k(int r) { return (r / kRpb) % kCpr; }
-  __device__ static int v(int r) { return 4 * ((r / kRpb) % (kCpr / 4)); }
-};
+using Swizzle = layout::FwdSwizzle<D>;
 
 // Global -> LDS without registers (buffer_load ... lds): this wave's share
 // of a BN x D tile starting at key j0.  Each instruction fills 1 KB of LDS
@@ -94,13 +85,12 @@ struct Swizzle {
 template <int D, int BN, bool IS_K>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile, int j0, int wq, int lane) {
   using C = FwdCfg<D, BN>;
-  using Z = Swizzle<D>;
-  constexpr int kRowsPerInst = 1024 / (2 * D);
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
     const int inst = wq * C::kDmaPerWave + i;
-    const int row = inst * kRowsPerInst + lane / Z::kCpr;
-    const int chunk = (lane % Z::kCpr) ^ (IS_K ? Z::k(row) : Z::v(row));
+    int row, chunk;
+    if constexpr (IS_K) layout::copy_slot(2 * D, inst, lane, Swizzle<D>::k, row, chunk);
+    else layout::copy_slot(2 * D, inst, lane, Swizzle<D>::v, row, chunk);
     const uint32_t goff = (uint32_t)((j0 + row) * D + 8 * chunk) * 2u;
     lds_copy16(r, goff, (uint32_t)(uintptr_t)(tile + inst * 512));
   }
@@ -300,17 +290,11 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // read): lane (s = lane % 16, G = bit 4, g = bit 5) reads row 4 g + s / 4
   // of each 8-row group at column 32 dm + 16 G + 4 (s % 4); f(row) depends
   // only on s / 4 because the group offsets are multiples of 8 rows.
-  using Z = Swizzle<D>;
   int koff[D / 16], voff[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lc * D + 8 * ((2 * ks + lg) ^ Z::k(lc));
-  {
-    const int sl = lane & 15, G = (lane >> 4) & 1;
-    const int row = 4 * lg + (sl >> 2);
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = layout::fwd_koff<D>(lc, lg, ks);
 #pragma unroll
-    for (int dm = 0; dm < D / 32; ++dm)
-      voff[dm] = row * D + 8 * ((4 * dm + 2 * G + ((sl & 3) >> 1)) ^ Z::v(row)) + 4 * (sl & 1);
-  }
+  for (int dm = 0; dm < D / 32; ++dm) voff[dm] = layout::fwd_voff<D>(lane, dm);
 
   const int q_wave0 = qt * C::BM + wave * 32;
   const int q_idx = q_wave0 + lc;

@@ -34,6 +34,7 @@
 //     adjacent chunks) hit distinct banks.
 #include "fa_common.h"
 #include "fa_internal.h"
+#include "fa_layout.h"
 
 namespace fa {
 
@@ -73,23 +74,10 @@ struct Fp8Cfg {
   static_assert(kThreads == 512, "kernel launch bounds assume 512 threads");
 };
 
-// Chunk permutation of row r (16-byte chunks; kCpr per row, kRps rows per
-// 256-byte bank sweep).
+// Chunk permutations of the K and V tiles and the key order of S^T's rows
+// (layout::Fp8Swizzle, layout::fp8_kperm).
 template <int D>
-struct Fp8Swizzle {
-  static constexpr int kCpr = D / 16;
-  static constexpr int kRps = 256 / D;
-  // K: the 16 rows one 16-lane read covers differ in (r % kRps, k(r)).
-  __device__ static int k(int r) { return ((r / kRps) & (kCpr / 2 - 1)) | (((r >> 4) & 1) * (kCpr / 2)); }
-  // V: 8 consecutive rows differ in (r % kRps, v(r)), and v(r) is even so
-  // the two adjacent chunks a 32-lane read covers stay apart.
-  __device__ static int v(int r) { return 2 * ((r / kRps) % (8 / kRps)); }
-};
-
-// Key (within a 32-key block) that row rho of the S^T product holds.
-__device__ __forceinline__ int kperm(int rho) {
-  return (((rho >> 2) & 1) << 4) | (((rho >> 3) & 3) << 2) | (rho & 3);
-}
+using Fp8Swizzle = layout::Fp8Swizzle<D>;
 
 // This wave's share of a BN x D byte tile starting at key j0, global -> LDS
 // (buffer_load ... lds, 1 KB per instruction in lane order); lane i loads the
@@ -98,13 +86,12 @@ __device__ __forceinline__ int kperm(int rho) {
 template <int D, int BN, bool IS_K>
 __device__ __forceinline__ void dma_tile_fp8(__amdgpu_buffer_rsrc_t r, uint8_t* tile, int j0, int wq, int lane) {
   using C = Fp8Cfg<D, BN>;
-  using Z = Fp8Swizzle<D>;
-  constexpr int kRowsPerInst = 1024 / D;
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
     const int inst = wq * C::kDmaPerWave + i;
-    const int row = inst * kRowsPerInst + lane / Z::kCpr;
-    const int chunk = (lane % Z::kCpr) ^ (IS_K ? Z::k(row) : Z::v(row));
+    int row, chunk;
+    if constexpr (IS_K) layout::copy_slot(D, inst, lane, Fp8Swizzle<D>::k, row, chunk);
+    else layout::copy_slot(D, inst, lane, Fp8Swizzle<D>::v, row, chunk);
     const uint32_t goff = (uint32_t)((j0 + row) * D + 16 * chunk);
     lds_copy16(r, goff, (uint32_t)(uintptr_t)(tile + inst * 1024));
   }
@@ -236,7 +223,6 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
                   __bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int num_qt, float scale_log2,
                   float v_descale) {
   using C = Fp8Cfg<D, BN>;
-  using Z = Fp8Swizzle<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
 
   const int tid = threadIdx.x;
@@ -266,17 +252,12 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   // rows 16 lg + 0..7 (+8, +32, +40) of chunk 2 dm + G, lane s = lane % 16
   // addressing row s / 2, bytes 8 (s % 2).
   int koff[C::KS][2], voff[C::DM];
-  {
-    const int kr = kperm(lc);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+  for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) koff[ks][p] = kr * D + 16 * ((4 * ks + 2 * lg + p) ^ Z::k(kr));
-    const int sl = lane & 15, G = (lane >> 4) & 1;
-    const int row = 16 * lg + (sl >> 1);
+    for (int p = 0; p < 2; ++p) koff[ks][p] = layout::fp8_koff<D>(lc, lg, ks, p);
 #pragma unroll
-    for (int dm = 0; dm < C::DM; ++dm) voff[dm] = row * D + 16 * ((2 * dm + G) ^ Z::v(row)) + 8 * (sl & 1);
-  }
+  for (int dm = 0; dm < C::DM; ++dm) voff[dm] = layout::fp8_voff<D>(lane, dm);
 
   const int q_wave0 = qt * C::BM + wave * 32;
   const int q_idx = q_wave0 + lc;

@@ -1,0 +1,348 @@
+// Host-side check of the kernels' LDS tile index math, compiled from the
+// same header the kernels use (io_aware_tiled_attn_amd/csrc/fa_layout.h).
+// Test infrastructure: built into tests/_build/liblayout_check.so and called
+// from tests/test_layout_cpu.py; no kernel runs here.
+//
+// For every tile shape the kernels accept (and the wider shapes that were
+// tried and set aside), it checks
+//   * the global -> LDS copies: every LDS chunk of a tile is written once,
+//     every (row, chunk) of the tile's rows is fetched once, and no row lies
+//     outside the tile;
+//   * every MFMA operand read: in bounds, aligned, and returning the row
+//     and column the operand layout asks for once the chunk permutation the
+//     copies applied is undone;
+//   * the bank spread of each read instruction (the LDS serves 256 bytes a
+//     cycle: 16 lanes of a 16-byte read or 32 lanes of an 8-byte read); the
+//     degree (1 = conflict-free) is reported, and for the backward's tiles,
+//     designed conflict-free, a degree above 1 counts as a violation;
+//   * the LDS the launch reserves against the 160 KB of a CU.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../io_aware_tiled_attn_amd/csrc/fa_layout.h"
+
+namespace {
+
+using namespace fa::layout;
+
+struct Report {
+  int violations = 0;
+  std::string text;
+  void note(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    text += buf;
+    text += "\n";
+  }
+  void fail(const char* fmt, ...) {
+    ++violations;
+    if (violations > 40) return;   // enough to diagnose
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    text += "VIOLATION ";
+    text += buf;
+    text += "\n";
+  }
+};
+
+// A tile whose rows are row_bytes wide, written by copy instructions with
+// the permutation f.  Records which (row, chunk) each LDS chunk holds.
+template <typename F>
+struct Tile {
+  int rows, row_bytes, bytes;
+  F f;
+  std::vector<int> holder;   // per LDS chunk: row * chunks + chunk, or -1
+  Tile(int rows_, int row_bytes_, F f_) : rows(rows_), row_bytes(row_bytes_), bytes(rows_ * row_bytes_), f(f_) {}
+
+  // Run the copies: n_inst instructions of 64 lanes.
+  void copy(Report& rep, const char* what) {
+    const int cpr = row_bytes / 16;
+    holder.assign(bytes / 16, -1);
+    std::vector<int> fetched(rows * cpr, 0);
+    if (bytes % 1024 != 0) rep.fail("%s: tile of %d bytes is not whole 1 KB copies", what, bytes);
+    for (int inst = 0; inst < bytes / 1024; ++inst)
+      for (int lane = 0; lane < 64; ++lane) {
+        int row, chunk;
+        copy_slot(row_bytes, inst, lane, f, row, chunk);
+        const int dst = inst * 1024 + 16 * lane;
+        if (row < 0 || row >= rows || chunk < 0 || chunk >= cpr) {
+          rep.fail("%s: copy inst %d lane %d fetches row %d chunk %d outside the tile", what, inst, lane, row, chunk);
+          continue;
+        }
+        if (dst + 16 > bytes) rep.fail("%s: copy inst %d lane %d writes byte %d past the tile", what, inst, lane, dst);
+        // The permutation must put this chunk where the copy writes it.
+        if (dst != row * row_bytes + 16 * (chunk ^ f(row)))
+          rep.fail("%s: copy inst %d lane %d writes (row %d, chunk %d) to byte %d, the layout puts it at %d", what,
+                   inst, lane, row, chunk, dst, row * row_bytes + 16 * (chunk ^ f(row)));
+        if (holder[dst / 16] != -1) rep.fail("%s: LDS chunk %d written twice", what, dst / 16);
+        holder[dst / 16] = row * cpr + chunk;
+        fetched[row * cpr + chunk]++;
+      }
+    for (int i = 0; i < rows * cpr; ++i)
+      if (fetched[i] != 1) rep.fail("%s: (row %d, chunk %d) fetched %d times", what, i / cpr, i % cpr, fetched[i]);
+  }
+
+  // The element a read of `width` bytes at `byte` returns: checks bounds and
+  // alignment, then compares the (row, chunk, byte in chunk) that LDS chunk
+  // holds with the expected one.
+  void expect(Report& rep, const char* what, int byte, int width, int row, int chunk, int within) {
+    if (byte < 0 || byte + width > bytes) {
+      rep.fail("%s: read of %d bytes at %d outside the %d-byte tile", what, width, byte, bytes);
+      return;
+    }
+    if (byte % width != 0) rep.fail("%s: read of %d bytes at %d misaligned", what, width, byte);
+    const int cpr = row_bytes / 16;
+    const int h = holder[byte / 16];
+    if (h != row * cpr + chunk || byte % 16 != within)
+      rep.fail("%s: read at byte %d returns (row %d, chunk %d, +%d), wanted (row %d, chunk %d, +%d)", what, byte,
+               h / cpr, h % cpr, byte % 16, row, chunk, within);
+  }
+};
+
+template <typename F>
+Tile<F> make_tile(int rows, int row_bytes, F f) {
+  return Tile<F>(rows, row_bytes, f);
+}
+
+// Conflict degree of one read instruction: the LDS serves 256 bytes (64
+// banks of 4 bytes) per cycle, `per` lanes at a time; the degree is the
+// largest number of distinct words any bank must deliver in one group.
+int conflict_degree(const std::vector<int>& byte_of_lane, int width) {
+  const int per = 256 / width;
+  int worst = 1;
+  for (int g0 = 0; g0 < 64; g0 += per) {
+    std::vector<std::vector<int>> words(64);
+    for (int l = g0; l < g0 + per; ++l)
+      for (int w = 0; w < width / 4; ++w) {
+        const int word = byte_of_lane[l] / 4 + w;
+        auto& v = words[word % 64];
+        bool seen = false;
+        for (int x : v) seen |= x == word;
+        if (!seen) v.push_back(word);
+      }
+    for (auto& v : words)
+      if ((int)v.size() > worst) worst = (int)v.size();
+  }
+  return worst;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 forward, tiles of BN keys x D.
+// ---------------------------------------------------------------------------
+template <int D, int BN>
+void check_fwd(Report& rep, bool launched) {
+  char what[96];
+  using Z = FwdSwizzle<D>;
+  auto kf = [](int r) { return Z::k(r); };
+  auto vf = [](int r) { return Z::v(r); };
+  auto K = make_tile(BN, 2 * D, kf);
+  auto V = make_tile(BN, 2 * D, vf);
+  snprintf(what, sizeof what, "fwd bf16 D=%d BN=%d K copy", D, BN);
+  K.copy(rep, what);
+  snprintf(what, sizeof what, "fwd bf16 D=%d BN=%d V copy", D, BN);
+  V.copy(rep, what);
+  if ((BN * D * 2) % 4096 != 0) rep.fail("fwd bf16 D=%d BN=%d: a tile does not split over four waves", D, BN);
+  int kdeg = 1, vdeg = 1;
+  // K as the A operand of S^T = K Q^T: lane (lc, lg), k-step ks, 32-key block mb.
+  for (int ks = 0; ks < D / 16; ++ks)
+    for (int mb = 0; mb < BN / 32; ++mb) {
+      std::vector<int> at(64);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int lc = lane & 31, lg = lane >> 5;
+        at[lane] = 2 * (fwd_koff<D>(lc, lg, ks) + 32 * mb * D);
+        snprintf(what, sizeof what, "fwd bf16 D=%d BN=%d K read ks=%d mb=%d lane=%d", D, BN, ks, mb, lane);
+        K.expect(rep, what, at[lane], 16, 32 * mb + lc, 2 * ks + lg, 0);
+      }
+      const int d = conflict_degree(at, 16);
+      if (d > kdeg) kdeg = d;
+    }
+  // V^T as the A operand of O^T += V^T P^T: per 16-key step c the two
+  // transposing reads at rows 16 c and 16 c + 8.
+  for (int dm = 0; dm < D / 32; ++dm)
+    for (int c = 0; c < BN / 16; ++c)
+      for (int h = 0; h < 16; h += 8) {
+        std::vector<int> at(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int sl = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
+          at[lane] = 2 * (fwd_voff<D>(lane, dm) + (16 * c + h) * D);
+          snprintf(what, sizeof what, "fwd bf16 D=%d BN=%d V read dm=%d c=%d h=%d lane=%d", D, BN, dm, c, h, lane);
+          V.expect(rep, what, at[lane], 8, 16 * c + h + 4 * g + (sl >> 2), 4 * dm + 2 * G + ((sl & 3) >> 1),
+                   8 * (sl & 1));
+        }
+        const int d = conflict_degree(at, 8);
+        if (d > vdeg) vdeg = d;
+      }
+  // LDS of a launch: three K and three V buffers, then the sparse tile list
+  // (at most N / BN + 1 ints; N <= 65536 keeps it within 8 KB).
+  const int lds = 2 * 3 * BN * D * 2;
+  const bool fits = lds + 4 * (65536 / BN + 1) <= 160 * 1024;
+  if (launched && !fits)
+    rep.fail("fwd bf16 D=%d BN=%d: %d bytes of tiles plus the tile list exceed 160 KB", D, BN, lds);
+  rep.note("fwd bf16 D=%d BN=%d (%s): LDS %d B%s, K read conflict degree %d, V read degree %d", D, BN,
+           launched ? "launched" : "not launched", lds, fits ? "" : " (over 160 KB)", kdeg, vdeg);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 forward, tiles of BN keys x D bytes.
+// ---------------------------------------------------------------------------
+template <int D, int BN>
+void check_fp8(Report& rep, bool launched) {
+  char what[96];
+  using Z = Fp8Swizzle<D>;
+  auto kf = [](int r) { return Z::k(r); };
+  auto vf = [](int r) { return Z::v(r); };
+  auto K = make_tile(BN, D, kf);
+  auto V = make_tile(BN, D, vf);
+  snprintf(what, sizeof what, "fwd fp8 D=%d BN=%d K copy", D, BN);
+  K.copy(rep, what);
+  snprintf(what, sizeof what, "fwd fp8 D=%d BN=%d V copy", D, BN);
+  V.copy(rep, what);
+  if ((BN * D) % 4096 != 0) rep.fail("fwd fp8 D=%d BN=%d: a tile does not split over four waves", D, BN);
+  // The 32 S^T rows of a block must hold 32 distinct keys of the block.
+  {
+    int seen = 0;
+    for (int rho = 0; rho < 32; ++rho) seen |= 1 << fp8_kperm(rho);
+    if (seen != -1) rep.fail("fp8 key order of S^T rows is not a permutation of 32 keys");
+  }
+  int kdeg = 1, vdeg = 1;
+  for (int ks = 0; ks < D / 64; ++ks)
+    for (int p = 0; p < 2; ++p)
+      for (int mb = 0; mb < BN / 32; ++mb) {
+        std::vector<int> at(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int lc = lane & 31, lg = lane >> 5;
+          at[lane] = fp8_koff<D>(lc, lg, ks, p) + 32 * mb * D;
+          snprintf(what, sizeof what, "fwd fp8 D=%d BN=%d K read ks=%d p=%d mb=%d lane=%d", D, BN, ks, p, mb, lane);
+          K.expect(rep, what, at[lane], 16, 32 * mb + fp8_kperm(lc), 4 * ks + 2 * lg + p, 0);
+        }
+        const int d = conflict_degree(at, 16);
+        if (d > kdeg) kdeg = d;
+      }
+  // V^T operand of a 64-key step j: four transposing reads, 0, 8, 32 and 40
+  // rows below the lane's first row.
+  const int extra[4] = {0, 8, 32, 40};
+  for (int dm = 0; dm < D / 32; ++dm)
+    for (int j = 0; j < BN / 64; ++j)
+      for (int e = 0; e < 4; ++e) {
+        std::vector<int> at(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int sl = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
+          at[lane] = fp8_voff<D>(lane, dm) + (64 * j + extra[e]) * D;
+          snprintf(what, sizeof what, "fwd fp8 D=%d BN=%d V read dm=%d j=%d e=%d lane=%d", D, BN, dm, j, e, lane);
+          V.expect(rep, what, at[lane], 8, 64 * j + extra[e] + 16 * g + (sl >> 1), 2 * dm + G, 8 * (sl & 1));
+        }
+        const int d = conflict_degree(at, 8);
+        if (d > vdeg) vdeg = d;
+      }
+  const int lds = 2 * 3 * BN * D;
+  if (lds > 160 * 1024) rep.fail("fwd fp8 D=%d BN=%d: %d bytes of tiles exceed 160 KB", D, BN, lds);
+  rep.note("fwd fp8 D=%d BN=%d (%s): LDS %d B, K read conflict degree %d, V read degree %d", D, BN,
+           launched ? "launched" : "not launched", lds, kdeg, vdeg);
+}
+
+// ---------------------------------------------------------------------------
+// Backward, fp16 tiles of D columns: 128 resident rows, 32-row blocks.  The
+// kernels read with byte addresses built as (lane constant) XOR (32 ks) for
+// rows and (lane constant) XOR (64 dm) + 32 c D for columns; both forms are
+// checked against the plain formulas and the copies.
+// ---------------------------------------------------------------------------
+template <int D>
+void check_bwd(Report& rep, int rows) {
+  char what[96];
+  auto f = [](int r) { return bwd_swz<D>(r); };
+  auto T = make_tile(rows, 2 * D, f);
+  snprintf(what, sizeof what, "bwd D=%d rows=%d copy", D, rows);
+  T.copy(rep, what);
+  int rdeg = 1, tdeg = 1;
+  for (int rb = 0; rb < rows; rb += 32)
+    for (int ks = 0; ks < D / 16; ++ks) {
+      std::vector<int> at(64);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int lc = lane & 31, lg = lane >> 5;
+        const int fast = (int)((2u * (unsigned)bwd_chunk_off<D>(lc, lg)) ^ (32u * ks)) + 2 * rb * D;
+        at[lane] = 2 * bwd_chunk_off<D>(rb + lc, 2 * ks + lg);
+        if (fast != at[lane])
+          rep.fail("bwd D=%d row read rb=%d ks=%d lane=%d: XOR address %d != %d", D, rb, ks, lane, fast, at[lane]);
+        snprintf(what, sizeof what, "bwd D=%d rows=%d row read rb=%d ks=%d lane=%d", D, rows, rb, ks, lane);
+        T.expect(rep, what, at[lane], 16, rb + lc, 2 * ks + lg, 0);
+      }
+      const int d = conflict_degree(at, 16);
+      if (d > rdeg) rdeg = d;
+    }
+  for (int r16 = 0; r16 < rows; r16 += 16)
+    for (int h = 0; h < 16; h += 8)
+      for (int dm = 0; dm < D / 32; ++dm) {
+        std::vector<int> at(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int s = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
+          const unsigned lc0 = 2u * (unsigned)bwd_tr_off<D>(lane, h, 0);
+          const int fast = (int)((lc0 ^ (64u * dm)) + 32u * (unsigned)(r16 / 16) * D);
+          at[lane] = 2 * bwd_tr_off<D>(lane, r16 + h, dm);
+          if (fast != at[lane])
+            rep.fail("bwd D=%d column read r=%d h=%d dm=%d lane=%d: XOR address %d != %d", D, r16, h, dm, lane, fast,
+                     at[lane]);
+          snprintf(what, sizeof what, "bwd D=%d rows=%d column read r=%d h=%d dm=%d lane=%d", D, rows, r16, h, dm,
+                   lane);
+          T.expect(rep, what, at[lane], 8, r16 + h + 4 * g + (s >> 2), 4 * dm + 2 * G + ((s & 3) >> 1), 8 * (s & 1));
+        }
+        const int d = conflict_degree(at, 8);
+        if (d > tdeg) tdeg = d;
+      }
+  if (rdeg > 1 || tdeg > 1)
+    rep.fail("bwd D=%d rows=%d: bank conflicts (row reads %d, column reads %d)", D, rows, rdeg, tdeg);
+  rep.note("bwd D=%d rows=%d: row read conflict degree %d, column read degree %d", D, rows, rdeg, tdeg);
+}
+
+// LDS the backward launches reserve: dK/dV kernel (resident K, V; two
+// buffers of Q, dO and row terms per group; or the closing sum) and dQ
+// kernel (three K, V buffers per group; or its closing sum), each plus the
+// sparse block list (at most N / 32 + 1 ints, N <= 65536).
+template <int D>
+void check_bwd_lds(Report& rep) {
+  const int res = 2 * 128 * D * 2, stage = 2 * 32 * D * 2 + 32 * 8, red = D * 4 * 64 * 4;
+  const int dkdv = (res + 4 * stage > red ? res + 4 * stage : red) + 4 * (65536 / 32 + 1);
+  const int dq = (6 * 2 * 32 * D * 2 > red / 2 ? 6 * 2 * 32 * D * 2 : red / 2) + 4 * (65536 / 32 + 1);
+  if (dkdv > 160 * 1024) rep.fail("bwd D=%d: dK/dV kernel LDS %d B exceeds 160 KB", D, dkdv);
+  if (dq > 160 * 1024) rep.fail("bwd D=%d: dQ kernel LDS %d B exceeds 160 KB", D, dq);
+  rep.note("bwd D=%d: LDS at most %d B (dK/dV), %d B (dQ)", D, dkdv, dq);
+}
+
+}  // namespace
+
+extern "C" int fa_layout_check(char* out, int out_len) {
+  Report rep;
+  // Launched tile widths, and the wider ones that were tried and set aside
+  // (d = 64 with 96 and 128 keys, FP8 with 128 keys).
+  check_fwd<64, 32>(rep, true);
+  check_fwd<64, 64>(rep, true);
+  check_fwd<64, 96>(rep, false);
+  check_fwd<64, 128>(rep, false);
+  check_fwd<128, 32>(rep, true);
+  check_fwd<128, 64>(rep, true);
+  check_fwd<128, 96>(rep, true);
+  check_fwd<128, 128>(rep, false);
+  check_fp8<64, 64>(rep, true);
+  check_fp8<64, 128>(rep, false);
+  check_fp8<128, 64>(rep, true);
+  check_fp8<128, 128>(rep, false);
+  check_bwd<64>(rep, 32);
+  check_bwd<64>(rep, 128);
+  check_bwd<128>(rep, 32);
+  check_bwd<128>(rep, 128);
+  check_bwd_lds<64>(rep);
+  check_bwd_lds<128>(rep);
+  if (out && out_len > 0) {
+    strncpy(out, rep.text.c_str(), (size_t)out_len - 1);
+    out[out_len - 1] = 0;
+  }
+  return rep.violations;
+}
