@@ -545,13 +545,17 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) pw[i] = dsw[i] = 0u;
 
-  // The group's buffers start as zeros (finite operands for the products a
-  // group runs without a block); then the group's first block, and the
-  // resident K, V times their factors as fp16, into LDS and (rows below N)
-  // into the fp16 copies the dQ kernel reads.
-  for (int i = gt; i < 2 * C::kStageBytes / 16; i += 256) ((u32x4*)gstage)[i] = (u32x4){0u, 0u, 0u, 0u};
-  __syncthreads();
+  // The group's first block into buffer 0; zeros into the buffers a round
+  // reads before any block was copied there (buffer 1 in round 0's gradient
+  // products, buffer 0 when the group has no block): finite operands for
+  // the products a group runs without a block.  Then the resident K, V
+  // times their factors as fp16, into LDS (the kernel copies them on to the
+  // workspace for the dQ kernel at its end, so no wait here covers those
+  // stores).
   if (valid(0)) stage(0, 0);
+  for (int b = valid(0) ? 1 : 0; b < 2; ++b)
+    for (int i = gt; i < C::kStageBytes / 16; i += 256)
+      ((u32x4*)(gstage + b * C::kStageBytes))[i] = (u32x4){0u, 0u, 0u, 0u};
   {
     constexpr int kChunks = C::RES * D / 8 / C::kThreads;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_off, (uint32_t)N * D * 2u);
@@ -567,15 +571,9 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int c = tid + i * C::kThreads, row = c / (D / 8), ch = c % (D / 8);
-      const u32x4 k16 = bf16x8_to_f16x8(kx[i], sk), v16 = bf16x8_to_f16x8(vx[i], sv);
       const int lo = bwd_chunk_off<D>(row, ch);
-      *(u32x4*)(Ks + lo) = k16;
-      *(u32x4*)(Vs + lo) = v16;
-      if (k0 + row < N) {
-        const size_t go = head_off + (size_t)(k0 + row) * D + 8 * ch;
-        *(u32x4*)(K16 + go) = k16;
-        *(u32x4*)(V16 + go) = v16;
-      }
+      *(u32x4*)(Ks + lo) = bf16x8_to_f16x8(kx[i], sk);
+      *(u32x4*)(Vs + lo) = bf16x8_to_f16x8(vx[i], sv);
     }
   }
   wait_vmem_all();
@@ -629,41 +627,57 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
   }
   if (g == 0) __syncthreads();
 
-  // Sum the two groups' dK^T and dV^T through LDS (feature-major, so
-  // consecutive lanes touch consecutive words), then store dK = scale dK^T
-  // and dV = dV^T in the inputs' units as bf16 rows of this lane's key.
-  float* red = (float*)smem_raw;
-  auto red_at = [&](int j) { return red + ((size_t)j * 4 + kb) * 64 + lane; };
-  if (g == 1) {
+  // The fp16 K, V rows of the tile (rows below N) on to the workspace for
+  // the dQ kernel; the closing sum below reuses this LDS.
+  {
+    constexpr int kChunks = C::RES * D / 8 / C::kThreads;
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        *red_at(16 * dm + i) = dk_acc[dm][i];
-        *red_at(D / 2 + 16 * dm + i) = dv_acc[dm][i];
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + i * C::kThreads, row = c / (D / 8), ch = c % (D / 8);
+      if (k0 + row < N) {
+        const int lo = bwd_chunk_off<D>(row, ch);
+        const size_t go = head_off + (size_t)(k0 + row) * D + 8 * ch;
+        *(u32x4*)(K16 + go) = *(const u32x4*)(Ks + lo);
+        *(u32x4*)(V16 + go) = *(const u32x4*)(Vs + lo);
       }
+    }
   }
   __syncthreads();
-  if (g == 0 && key_ok) {
+
+  // Close: the two groups' partial dK^T and dV^T are summed through LDS.
+  // Group 0 finishes dK and group 1 dV: each writes the other's partial,
+  // 16 bytes per lane and instruction with consecutive lanes on consecutive
+  // chunks, then adds the one it finishes.  Stored as dK = scale dK^T and
+  // dV = dV^T in the inputs' units, bf16 rows of this lane's key.
+  // red_at(t, c): chunk c (accumulator registers 4 (c % 4) .. + 3 of
+  // feature block c / 4) of tensor t (0 dK, 1 dV) of key block kb.
+  f32x4* red = (f32x4*)smem_raw;
+  auto red_at = [&](int t, int c) { return red + (((size_t)t * (D / 8) + c) * 4 + kb) * 64 + lane; };
+  // (The branches on g keep every register index a constant.)
+  auto put = [&](const f32x16 (&a)[DM], int t) {
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm)
+    for (int c = 0; c < D / 8; ++c)
+      *red_at(t, c) = (f32x4){a[c / 4][4 * (c % 4)], a[c / 4][4 * (c % 4) + 1], a[c / 4][4 * (c % 4) + 2],
+                              a[c / 4][4 * (c % 4) + 3]};
+  };
+  auto finish = [&](const f32x16 (&a)[DM], int t, float fac, __bf16* out) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dk_acc[dm][i] += *red_at(16 * dm + i);
-        dv_acc[dm][i] += *red_at(D / 2 + 16 * dm + i);
-      }
+    for (int c = 0; c < D / 8; ++c) {
+      const f32x4 b = *red_at(t, c);
+      const int dm = c / 4, r0 = 4 * (c % 4);
+      // Registers r0 .. r0 + 3 of block dm hold features 32 dm + 8 (r0 / 4) + 4 lg + 0..3.
+      *(u32x2*)(out + 32 * dm + 8 * (c % 4) + 4 * lg) =
+          (u32x2){pack_bf16x2((a[dm][r0] + b[0]) * fac, (a[dm][r0 + 1] + b[1]) * fac),
+                  pack_bf16x2((a[dm][r0 + 2] + b[2]) * fac, (a[dm][r0 + 3] + b[3]) * fac)};
+    }
+  };
+  if (g == 0) put(dv_acc, 1);
+  else put(dk_acc, 0);
+  __syncthreads();
+  if (key_ok) {
     const size_t row = ((size_t)bh * N + key) * D;
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 wk = {pack_bf16x2(dk_acc[dm][4 * i] * dk_fac, dk_acc[dm][4 * i + 1] * dk_fac),
-                    pack_bf16x2(dk_acc[dm][4 * i + 2] * dk_fac, dk_acc[dm][4 * i + 3] * dk_fac)};
-        u32x2 wv = {pack_bf16x2(dv_acc[dm][4 * i] * dv_fac, dv_acc[dm][4 * i + 1] * dv_fac),
-                    pack_bf16x2(dv_acc[dm][4 * i + 2] * dv_fac, dv_acc[dm][4 * i + 3] * dv_fac)};
-        *(u32x2*)(dK + row + 32 * dm + 8 * i + 4 * lg) = wk;
-        *(u32x2*)(dV + row + 32 * dm + 8 * i + 4 * lg) = wv;
-      }
+    if (g == 0) finish(dk_acc, 0, dk_fac, dK + row);
+    else finish(dv_acc, 1, dv_fac, dV + row);
   }
 }
 
@@ -764,12 +778,16 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) dsw[i] = 0u;
 
-  // The group's buffers start as zeros (finite operands for the products a
-  // group runs without a block), then take its first two blocks.
-  for (int i = gt; i < 3 * C::kDqStageBytes / 16; i += 256) ((u32x4*)gstage)[i] = (u32x4){0u, 0u, 0u, 0u};
-  __syncthreads();
+  // The group's first two blocks into buffers 0 and 1; zeros into the
+  // buffers a round reads before any block was copied there (buffer 2 in
+  // round 0's gradient products, buffers 0 and 1 when the group has no such
+  // block): finite operands for the products a group runs without a block.
   if (valid(0)) stage(0, 0);
   if (valid(1)) stage(1, 1);
+  for (int b = 0; b < 3; ++b)
+    if (b == 2 || !valid(b))
+      for (int i = gt; i < C::kDqStageBytes / 16; i += 256)
+        ((u32x4*)(gstage + b * C::kDqStageBytes))[i] = (u32x4){0u, 0u, 0u, 0u};
   wait_vmem_all();
   __syncthreads();
   if (g == 1) __syncthreads();
@@ -811,28 +829,43 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
   }
   if (g == 0) __syncthreads();
 
-  // Sum the two groups' dQ^T through LDS and store dQ = scale dQ^T in the
-  // inputs' units as bf16 rows of this lane's query.
-  float* red = (float*)smem_raw;
-  auto red_at = [&](int j) { return red + ((size_t)j * 4 + qb) * 64 + lane; };
-  if (g == 1) {
+  // Close: the two groups' partial dQ^T are summed through LDS, group 0
+  // finishing feature blocks 0 .. DM / 2 - 1 and group 1 the rest: each
+  // writes its partial of the other's half (16 bytes per lane and
+  // instruction, consecutive lanes on consecutive chunks), then adds the
+  // other's partial of its own half and stores dQ = scale dQ^T in the
+  // inputs' units as bf16 of this lane's query row.  red_at(c): chunk c
+  // (accumulator registers 4 (c % 4) .. + 3 of feature block c / 4) of
+  // query block qb.
+  f32x4* red = (f32x4*)smem_raw;
+  auto red_at = [&](int c) { return red + ((size_t)c * 4 + qb) * 64 + lane; };
+  constexpr int kHalf = D / 16;   // chunks per half
+  // (The branches on g keep every register index a constant.)
+  auto put = [&](int c0) {
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm)
+    for (int j = 0; j < kHalf; ++j) {
+      const int c = c0 + j;
+      *red_at(c) = (f32x4){dq_acc[c / 4][4 * (c % 4)], dq_acc[c / 4][4 * (c % 4) + 1], dq_acc[c / 4][4 * (c % 4) + 2],
+                           dq_acc[c / 4][4 * (c % 4) + 3]};
+    }
+  };
+  auto finish = [&](int c0) {
+    __bf16* out = dQ + ((size_t)bh * N + q) * D;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) *red_at(16 * dm + i) = dq_acc[dm][i];
-  }
+    for (int j = 0; j < kHalf; ++j) {
+      const int c = c0 + j, dm = c / 4, r0 = 4 * (c % 4);
+      const f32x4 b = *red_at(c);
+      *(u32x2*)(out + 32 * dm + 8 * (c % 4) + 4 * lg) =
+          (u32x2){pack_bf16x2((dq_acc[dm][r0] + b[0]) * dq_fac, (dq_acc[dm][r0 + 1] + b[1]) * dq_fac),
+                  pack_bf16x2((dq_acc[dm][r0 + 2] + b[2]) * dq_fac, (dq_acc[dm][r0 + 3] + b[3]) * dq_fac)};
+    }
+  };
+  if (g == 0) put(kHalf);
+  else put(0);
   __syncthreads();
-  if (g == 0 && q < N) {
-    const size_t row = ((size_t)bh * N + q) * D;
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = (dq_acc[dm][4 * i + j] + *red_at(16 * dm + 4 * i + j)) * dq_fac;
-        *(u32x2*)(dQ + row + 32 * dm + 8 * i + 4 * lg) = (u32x2){pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-      }
+  if (q < N) {
+    if (g == 0) finish(0);
+    else finish(kHalf);
   }
 }
 

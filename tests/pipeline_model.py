@@ -150,7 +150,6 @@ def dkdv_schedule(n_blk, bufs=2, copy_in_vector=True):
 
         def buf(r):
             return "g%d.%d" % (g_i, r % bufs)
-        g.barrier()                                     # after zeroing the buffers
         if has(0):
             g.copy(buf(0), (g_i, 0))
         g.wait("all")
@@ -188,7 +187,6 @@ def dq_schedule(n_blk, bufs=3, ahead=2):
 
         def buf(r):
             return "g%d.%d" % (g_i, r % bufs)
-        g.barrier()
         for r in range(ahead):
             if has(r):
                 g.copy(buf(r), (g_i, r))
