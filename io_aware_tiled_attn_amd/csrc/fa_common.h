@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_layout.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -180,6 +182,34 @@ __device__ __forceinline__ void xcd_head_major(int bid, int BH, int num_tiles, i
   } else {
     tile = bid / BH;
     bh = bid % BH;
+  }
+}
+
+// Forward epilogue: this wave's 32 output rows (queries q0 .. q0 + 31, the
+// O^T accumulators times inv_l rounded to bf16) staged through the wave's
+// own 64 D bytes of LDS at `stage` and written as whole rows, 1 KB of
+// consecutive rows per store instruction (instead of 16 bytes in each of
+// 32 rows).  Rows at or past N are skipped.  No other wave may use `stage`
+// meanwhile; the wave's LDS writes and reads stay in order.
+template <int D>
+__device__ __forceinline__ void store_o_rows(const f32x16 (&oacc)[D / 32], float inv_l, __bf16* stage,
+                                             __bf16* o_head, int q0, int N, int lane) {
+  const int lc = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int dm = 0; dm < D / 32; ++dm)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * inv_l, oacc[dm][4 * i + 1] * inv_l),
+                       pack_bf16x2(oacc[dm][4 * i + 2] * inv_l, oacc[dm][4 * i + 3] * inv_l)};
+      *(u32x2*)(stage + layout::fwd_ostage_off<D>(lc, lg, dm, i)) = w;
+    }
+  constexpr int kInst = 32 * D * 2 / 1024;
+#pragma unroll
+  for (int j = 0; j < kInst; ++j) {
+    int row, chunk;
+    layout::copy_slot(2 * D, j, lane, layout::FwdSwizzle<D>::k, row, chunk);
+    const u32x4 v = *(const u32x4*)(stage + j * 512 + 8 * lane);
+    if (q0 + row < N) *(u32x4*)(o_head + (size_t)(q0 + row) * D + 8 * chunk) = v;
   }
 }
 

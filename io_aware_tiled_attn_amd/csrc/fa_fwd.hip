@@ -13,9 +13,9 @@
 //     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so the
 //     32x32 accumulator puts one query per lane column: the row max and row
 //     sum are in-lane reductions plus one permlane32 swap.
-//   * K and V tiles of BN keys are copied into LDS (three buffers each)
-//     straight from global memory (buffer_load ... lds: no registers and no
-//     LDS write instructions) and shared by the 8 waves.  Each key-tile step has two barrier-separated
+//   * K and V tiles of BN keys are copied into LDS (three buffers each,
+//     three tiles ahead) straight from global memory (buffer_load ... lds:
+//     no registers and no LDS write instructions) and shared by the 8 waves.  Each key-tile step has two barrier-separated
 //     phases: a matrix phase (O += P(t) V(t) and S(t+1) = K(t+1) Q^T) and a
 //     vector phase (the online softmax of S(t+1)).  Waves 4-7 run one phase
 //     behind waves 0-3, so the two waves sharing a SIMD alternate between the
@@ -36,11 +36,11 @@
 //     reduction and makes the output rescale rare.
 //   * Global reads use buffer descriptors sized to the head: reads past the
 //     last row return zeros, so ragged tails need no branches.
-//   * Workgroups are issued heaviest first (causal), with all query tiles of
-//     one head on the same XCD (dispatch is round-robin over 8 XCDs and the
-//     head index is the fast-varying part of the workgroup id).  Keeping the
-//     global heaviest-first order beats working through one head at a time
-//     per XCD, even though the latter reads K and V from memory only once.
+//   * Workgroups are issued heaviest first (causal), all query tiles of a
+//     head on the same XCD, that XCD's heads taken in groups just large
+//     enough to fill it (xcd_head_groups): a group's tiles start together
+//     and walk the same K/V tiles in step, so most tile copies are served by
+//     the XCD's L2.
 #include "fa_common.h"
 #include "fa_internal.h"
 #include "fa_layout.h"
@@ -50,7 +50,7 @@ namespace fa {
 constexpr float kPSumLimit = 256.0f;
 constexpr int kSparseBlock = FA_SPARSE_BLOCK;   // block-mask granularity (queries and keys)
 #ifndef FWD_LOOKAHEAD
-#define FWD_LOOKAHEAD 8
+#define FWD_LOOKAHEAD 7
 #endif
 
 template <int D, int BN>
@@ -60,8 +60,11 @@ struct FwdCfg {
   static constexpr int BM = kWaves * 32;
   static constexpr int kTile = BN * D;     // bf16 elements per K or V tile (unpadded rows)
   static constexpr int kBufs = 3;          // LDS buffers per tensor
-  // LDS: K buffers 0..2 | V buffers 0..2
-  static constexpr int kLdsBytes = 2 * kBufs * kTile * 2;
+  // LDS: K buffers 0..2 | V buffers 0..2; after the loop the same bytes
+  // stage the output rows (32 x D bf16 per wave).
+  static constexpr int kTileBytes = 2 * kBufs * kTile * 2;
+  static constexpr int kStageBytes = kWaves * 32 * D * 2;
+  static constexpr int kLdsBytes = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
   // Each group of four waves copies one tensor; 1 KB per copy instruction.
   static constexpr int kDmaPerWave = kTile * 2 / 1024 / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
@@ -149,6 +152,22 @@ __device__ __forceinline__ float tile_exp(const f32x16 (&s)[BN / 32], bf16x8 (&p
       pb[2 * mb + h] = __builtin_bit_cast(bf16x8, ((u32x4){w[0], w[1], w[2], w[3]}));
     }
   return rowsum;
+}
+
+// The first tile of a row: the reference m is the tile's max (-inf when
+// every score is masked) and l is the tile's sum.  The same values as
+// softmax_step from m = -inf, l = 0, O = 0, without the exponentials taken
+// against m = -inf first.
+template <int BN>
+__device__ __forceinline__ void softmax_first(const f32x16 (&s)[BN / 32], bf16x8 (&pb)[BN / 16], float& m_run,
+                                              float& l_run, float scale_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  m_run = max_with_lane_xor32(mx) * scale_log2;
+  l_run = tile_exp<BN>(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
 }
 
 // Online-softmax step for one tile of scores (this lane's query column).
@@ -257,7 +276,8 @@ template <int D, int BN, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(512)
 fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                   const uint8_t* __restrict__ bmask, int N, int BH, int num_qt, float scale_log2) {
+                   const uint8_t* __restrict__ bmask, int N, int BH, int num_qt, int hg, int wpx,
+                   float scale_log2) {
   using C = FwdCfg<D, BN>;
   static_assert(!SPARSE || (C::BM == 2 * kSparseBlock && kSparseBlock % BN == 0), "sparse blocks vs tiles");
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
@@ -265,25 +285,22 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int group = wave >> 2;   // 0: waves 0-3 (one per SIMD), 1: waves 4-7
-  const int lane = tid & 63;
-  const int lc = lane & 31;      // lane column: query within the wave
-  const int lg = lane >> 5;      // lane half
   const int wq = wave & 3;       // wave within its group
 
-  const int bid = blockIdx.x;
-  const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
-  const int bh = bid % BH;
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
-  // Group 0 copies the K tiles into LDS, group 1 the V tiles.
-  const __amdgpu_buffer_rsrc_t rmine = make_rsrc((group == 0 ? K : V) + head_off, head_bytes);
-  auto kbuf = [&](int i) { return smem + i * C::kTile; };
-  auto vbuf = [&](int i) { return smem + (C::kBufs + i) * C::kTile; };
-  auto copy_tile = [&](int tile, int buf) {
-    if (group == 0) dma_tile<D, BN, true>(rmine, kbuf(buf), tile * BN, wq, lane);
-    else dma_tile<D, BN, false>(rmine, vbuf(buf), tile * BN, wq, lane);
-  };
+  // One (head, 256-query tile) item per pass.  wpx = 0: this workgroup's
+  // single item, heaviest query tiles first with heads grouped per XCD.
+  // wpx > 0 (persistent launch, wpx workgroups per XCD): the workgroup works
+  // through its share of its XCD's list of items.
+  const int xcd_items = BH / 8 * num_qt;
+  for (int pass = 0;; ++pass) {
+  // The lane index enters each pass as a fresh value, so the per-lane
+  // address arithmetic of the pass is done inside it rather than hoisted out
+  // of the item loop and held in registers through every step.
+  int lane_v = tid & 63;
+  asm volatile("" : "+v"(lane_v));
+  const int lane = lane_v;
+  const int lc = lane & 31;      // lane column: query within the wave
+  const int lg = lane >> 5;      // lane half
 
   // This lane's swizzled LDS offsets.  K (A operand of S^T = K Q^T): row lc,
   // chunk 2 ks + lg.  V (A operand of O^T += V^T P^T via the transposing
@@ -295,6 +312,27 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = layout::fwd_koff<D>(lc, lg, ks);
 #pragma unroll
   for (int dm = 0; dm < D / 32; ++dm) voff[dm] = layout::fwd_voff<D>(lane, dm);
+
+  int qt, bh;
+  if (wpx > 0) {
+    const int k = layout::persistent_item(blockIdx.x >> 3, pass, wpx, xcd_items);
+    if (k < 0) break;
+    layout::xcd_item(blockIdx.x & 7, k, num_qt, hg, bh, qt);
+  } else {
+    if (pass > 0) break;
+    layout::xcd_head_groups(blockIdx.x, BH, num_qt, hg, bh, qt);
+  }
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
+  // Group 0 copies the K tiles into LDS, group 1 the V tiles.
+  const __amdgpu_buffer_rsrc_t rmine = make_rsrc((group == 0 ? K : V) + head_off, head_bytes);
+  auto kbuf = [&](int i) { return smem + i * C::kTile; };
+  auto vbuf = [&](int i) { return smem + (C::kBufs + i) * C::kTile; };
+  auto copy_tile = [&](int tile, int buf) {
+    if (group == 0) dma_tile<D, BN, true>(rmine, kbuf(buf), tile * BN, wq, lane);
+    else dma_tile<D, BN, false>(rmine, vbuf(buf), tile * BN, wq, lane);
+  };
 
   const int q_wave0 = qt * C::BM + wave * 32;
   const int q_idx = q_wave0 + lc;
@@ -319,7 +357,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // Sparse: list of visited key tiles, entry = tile | keep(block 0) << 24 |
   // keep(block 1) << 25, built by wave 0 with a ballot compaction.
-  int* tlist = (int*)(smem + 2 * C::kBufs * C::kTile);   // [0] = count, then entries
+  int* tlist = (int*)(smem + 2 * C::kBufs * C::kTile);   // after the tiles: [0] = count, then entries
   if constexpr (SPARSE) {
     const int nb = (N + kSparseBlock - 1) / kSparseBlock;
     const uint8_t* row0 = bmask + ((size_t)bh * nb + 2 * qt) * nb;
@@ -353,6 +391,9 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (num_kt > 1) copy_tile(tile_at(1), 1);
   wait_vmem_all();
   __syncthreads();
+  // The third, into the still unused buffer 2; waited for at the end of the
+  // first vector phase.
+  if (num_kt > 2) copy_tile(tile_at(2), 2);
 
   f32x16 s[BN / 32];
   bf16x8 pb[BN / 16];
@@ -375,7 +416,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (num_kt > 0) {
     score_tile<D, BN>(s, kbuf(0), koff, qb);
     mask_visit(0);
-    softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+    softmax_first<BN>(s, pb, m_run, l_run, scale_log2);
   }
 
   // The two waves on each SIMD (waves w and w + 4) alternate: group 1 runs
@@ -383,12 +424,17 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // MFMAs the other is in its exponentials.  Every wave passes the same
   // number of barriers (group 1 one extra here, group 0 one extra at the
   // end).  Step t works on visited tiles t and t+1 (all key tiles in
-  // order, dense).  At the start of its matrix phase of step t each group
-  // starts the copy of visited tile t+2 of its tensor into buffer (t+2) % 3,
-  // and waits for it at the end of its vector phase of the same step.  That
-  // buffer's previous tile (t-1) was last read at least one barrier before
-  // the copy starts, and the new tile is first read at least one barrier
-  // after the wait.
+  // order, dense).  At the start of its vector phase of step t each group
+  // starts the copy of visited tile t+3 of its tensor into buffer t % 3, and
+  // at the end of that phase waits for all its copies but that one.  Tile
+  // t's last reads (K(t) by both groups' score products of step t-1, V(t)
+  // by the P V products of step t, group 1's being the later) end at least
+  // one barrier before the copy starts.  Tile t+3 is first read in step
+  // t+2 (K(t+3) by group 0's score product, V(t+3) by the operand reads
+  // that end the vector phase before it), at least one barrier after the
+  // wait of step t+1 that completes it; the copy has three barrier
+  // intervals to land, which covers the latency of a tile read that the
+  // L2 does not hold.
   constexpr bool kPreload = D == 128;
   static_assert(!kPreload || FWD_LOOKAHEAD <= BN / 16 * (D / 32), "preloaded products must all be P V products");
   bf16x8 ring[FWD_LOOKAHEAD];
@@ -398,8 +444,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   int b_cur = 0;   // t % 3
   for (int t = 0; t < num_kt; ++t) {
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;    // (t + 1) % 3
-    const int b_copy = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
-    if (t + 2 < num_kt) copy_tile(tile_at(t + 2), b_copy);
+    const int b_after = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
     // wave runs the same instruction stream on every step: on causal tiles
     // wholly above a wave's queries its P is all zero (the tile is masked
@@ -408,34 +453,33 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1).
+    const bool copy_next = t + 3 < num_kt;
+    if (copy_next) copy_tile(tile_at(t + 3), b_cur);
     if (t + 1 < num_kt) {
       mask_visit(t + 1);
       softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
       // V(t+1)'s copy was waited for at the end of the previous step, so the
       // barrier before this phase published it.
-      if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(b_next), voff, kbuf(b_copy), koff);
+      if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(b_next), voff, kbuf(b_after), koff);
     }
-    wait_vmem_all();
+    if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
+    else wait_vmem_all();
     __syncthreads();
     b_cur = b_next;
   }
   if (group == 0) __syncthreads();
 
-  // Epilogue: O / l rounded to bf16, and LSE = m + ln l (natural log).
+  // Epilogue: O / l rounded to bf16, and LSE = m + ln l (natural log).  The
+  // last barrier above follows every wave's last tile read, so the tile
+  // buffers are free to stage the output rows.
   const float l_tot = sum_with_lane_xor32(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_idx < N) {
-    __bf16* orow = O + head_off + (size_t)q_idx * D;
-#pragma unroll
-    for (int dm = 0; dm < D / 32; ++dm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * inv_l, oacc[dm][4 * i + 1] * inv_l),
-                   pack_bf16x2(oacc[dm][4 * i + 2] * inv_l, oacc[dm][4 * i + 3] * inv_l)};
-        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * lg) = w;
-      }
-    if (LSE != nullptr && lg == 0)
-      LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+  store_o_rows<D>(oacc, inv_l, smem + wave * 32 * D, O + head_off, q_wave0, N, lane);
+  if (LSE != nullptr && lg == 0 && q_idx < N)
+    LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+  // Every wave's staged output rows are read back before the next item's
+  // first copies (and sparse list) overwrite the LDS.
+  if (wpx > 0) __syncthreads();
   }
 }
 
@@ -532,14 +576,18 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   // The sparse kernel keeps its list of visited key tiles (count first)
   // after the tile buffers.
   const int list_bytes = SPARSE ? ((4 * ((a.N + BN - 1) / BN + 1) + 15) & ~15) : 0;
-  const int lds = C::kLdsBytes + list_bytes;
+  const int lds = C::kTileBytes + list_bytes > C::kLdsBytes ? C::kTileBytes + list_bytes : C::kLdsBytes;
   // Dynamic LDS above 64 KB must be allowed explicitly; setting the same
   // value from several threads is harmless.
-  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q,
-                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, (const uint8_t*)a.bmask, a.N, BH,
-                     num_qt, a.scale * kLog2e);
+  int hg = 0, wpx = 0;
+  e = forward_work_layout((const void*)kern, C::kThreads, lds, BH, num_qt, &hg, &wpx);
+  if (e != hipSuccess) return e;
+  const int grid = wpx > 0 ? 8 * wpx : num_qt * BH;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
+                     (const __bf16*)a.v, (__bf16*)a.o, a.lse, (const uint8_t*)a.bmask, a.N, BH, num_qt, hg, wpx,
+                     a.scale * kLog2e);
   return hipGetLastError();
 }
 

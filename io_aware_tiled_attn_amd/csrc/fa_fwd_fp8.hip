@@ -60,7 +60,11 @@ struct Fp8Cfg {
   static constexpr int NC = BN / 64;       // 64-key chunks per tile: the k of one P V product
   static constexpr int kTile = BN * D;     // bytes of one K or V tile
   static constexpr int kBufs = 3;
-  static constexpr int kLdsBytes = 2 * kBufs * kTile;
+  // K buffers 0..2 | V buffers 0..2; after the loop the same bytes stage the
+  // output rows (32 x D bf16 per wave).
+  static constexpr int kTileBytes = 2 * kBufs * kTile;
+  static constexpr int kStageBytes = kWaves * 32 * D * 2;
+  static constexpr int kLdsBytes = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
   static constexpr int kDmaPerWave = kTile / 1024 / 4;   // 1 KB copies per wave and tile
   static constexpr int KS = D / 64;        // k-steps of S^T = K Q^T
   static constexpr int DM = D / 32;        // 32-feature blocks of O^T
@@ -177,6 +181,21 @@ __device__ __forceinline__ void softmax_step_fp8(const f32x16 (&s)[BN / 32], i32
   l_run += rs;
 }
 
+// The first tile of a row: m is the tile's max, l the tile's sum (the values
+// softmax_step_fp8 reaches from m = -inf, l = 0, O = 0, without its first
+// pass of exponentials against m = -inf).
+template <int BN>
+__device__ __forceinline__ void softmax_first_fp8(const f32x16 (&s)[BN / 32], i32x8 (&pb)[BN / 64], float& m_run,
+                                                  float& l_run, float scale_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < BN / 32; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  m_run = max_with_lane_xor32(mx) * scale_log2;
+  l_run = tile_exp_fp8<BN>(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
+}
+
 // One matrix phase: O^T += V^T(t) P^T(t) (NC DM products) then
 // S^T(t+1) = K(t+1) Q^T (NB KS products), one MFMA stream with the LDS
 // operands read L products ahead.
@@ -220,8 +239,8 @@ __device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i
 template <int D, int BN, bool CAUSAL>
 __global__ void __launch_bounds__(512)
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
-                  __bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int num_qt, float scale_log2,
-                  float v_descale) {
+                  __bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int num_qt, int hg,
+                  float scale_log2, float v_descale) {
   using C = Fp8Cfg<D, BN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
 
@@ -233,9 +252,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   const int lg = lane >> 5;
   const int wq = wave & 3;
 
-  const int bid = blockIdx.x;
-  const int qt = num_qt - 1 - bid / BH;   // heaviest query tiles first
-  const int bh = bid % BH;
+  int qt, bh;   // heaviest query tiles first, heads grouped per XCD
+  layout::xcd_head_groups(blockIdx.x, BH, num_qt, hg, bh, qt);
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
@@ -287,6 +305,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   if (num_kt > 1) copy_tile(1, 1);
   wait_vmem_all();
   __syncthreads();
+  if (num_kt > 2) copy_tile(2, 2);
 
   f32x16 s[C::NB];
   i32x8 pb[C::NC];
@@ -299,47 +318,39 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
       for (int mb = 0; mb < C::NB; ++mb)
         s[mb] = mfma32_fp8(lds_k_operand(kbuf(0) + 32 * mb * D, koff[ks][0], koff[ks][1]), qb[ks], s[mb]);
     if (masked(0)) mask_tile_fp8<BN>(s, 0, qlim, lg);
-    softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+    softmax_first_fp8<BN>(s, pb, m_run, l_run, scale_log2);
   }
 
   // Ping-pong and copy schedule as in the bf16 kernel: group 1 runs one
-  // barrier interval behind group 0; tile t + 2 is copied into buffer
-  // (t + 2) % 3 during step t and waited for at the end of the step's
-  // vector phase.
+  // barrier interval behind group 0; tile t + 3 is copied into buffer t % 3
+  // from the start of step t's vector phase, and at that phase's end each
+  // wave waits for all its copies but that one.
   if (group == 1) __syncthreads();
   int b_cur = 0;
   for (int t = 0; t < num_kt; ++t) {
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;
-    const int b_copy = b_cur == 0 ? 2 : b_cur - 1;
-    if (t + 2 < num_kt) copy_tile(t + 2, b_copy);
     matrix_phase_fp8<D, BN, 3>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
+    const bool copy_next = t + 3 < num_kt;
+    if (copy_next) copy_tile(t + 3, b_cur);
     if (t + 1 < num_kt) {
       if (masked(t + 1)) mask_tile_fp8<BN>(s, (t + 1) * BN, qlim, lg);
       softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     }
-    wait_vmem_all();
+    if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
+    else wait_vmem_all();
     __syncthreads();
     b_cur = b_next;
   }
   if (group == 0) __syncthreads();
 
-  // O = O^T / l * v_descale as bf16; LSE = m ln 2 + ln l.
+  // O = O^T / l * v_descale as bf16, staged through the (now free) tile
+  // buffers; LSE = m ln 2 + ln l.
   const float l_tot = sum_with_lane_xor32(l_run);
   const float f = l_tot > 0.f ? v_descale / l_tot : 0.f;
-  if (q_idx < N) {
-    __bf16* orow = O + head_off + (size_t)q_idx * D;
-#pragma unroll
-    for (int dm = 0; dm < C::DM; ++dm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * f, oacc[dm][4 * i + 1] * f),
-                   pack_bf16x2(oacc[dm][4 * i + 2] * f, oacc[dm][4 * i + 3] * f)};
-        *(u32x2*)(orow + 32 * dm + 8 * i + 4 * lg) = w;
-      }
-    if (LSE != nullptr && lg == 0)
-      LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
-  }
+  store_o_rows<D>(oacc, f, (__bf16*)smem8 + wave * 32 * D, O + head_off, q_wave0, N, lane);
+  if (LSE != nullptr && lg == 0 && q_idx < N)
+    LSE[(size_t)bh * N + q_idx] = l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
@@ -349,11 +360,13 @@ static hipError_t launch_fp8_d(const FwdFp8Args& a) {
   const int BH = a.B * a.H;
   const int num_qt = (a.N + C::BM - 1) / C::BM;
   auto kern = fa_fwd_fp8_kernel<D, BN, CAUSAL>;
-  const hipError_t e =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  if (e != hipSuccess) return e;
+  int hg = 0, wpx = 0;
+  e = forward_work_layout((const void*)kern, C::kThreads, C::kLdsBytes, BH, num_qt, &hg, &wpx);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(num_qt * BH), dim3(C::kThreads), C::kLdsBytes, a.stream, (const uint8_t*)a.q,
-                     (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o, a.lse, a.N, BH, num_qt,
+                     (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o, a.lse, a.N, BH, num_qt, hg,
                      a.scale * a.q_descale * a.k_descale * kLog2e, a.v_descale);
   return hipGetLastError();
 }

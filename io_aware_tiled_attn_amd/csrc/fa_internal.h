@@ -6,6 +6,7 @@
 #include <stddef.h>
 
 #include "../../include/flash_attn.h"
+#include "fa_layout.h"
 
 namespace fa {
 
@@ -36,6 +37,29 @@ struct FwdFp8Args {
   int causal;
   hipStream_t stream;
 };
+
+// Work layout of a forward launch of `kern` over num_qt query tiles x BH
+// heads, from the workgroups one XCD runs at once (occupancy x compute
+// units / 8 XCDs): hg, the heads per XCD group (layout::xcd_head_groups;
+// 0 when BH is not a multiple of 8), and wpx, the workgroups per XCD of a
+// persistent launch (layout::persistent_item; 0 for one workgroup per item,
+// the launch used when hg is 0).
+inline hipError_t forward_work_layout(const void* kern, int threads, int lds, int BH, int num_qt, int* hg,
+                                      int* wpx) {
+  *hg = 0;
+  *wpx = 0;
+  if (BH % 8 != 0) return hipSuccess;
+  int occ = 0, dev = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, (size_t)lds);
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int resident = occ * cus / 8;
+  *hg = layout::head_group_size(resident, BH, num_qt);
+  const int items = BH / 8 * num_qt;
+  *wpx = resident < 1 ? 0 : (resident < items ? resident : items);
+  return hipSuccess;
+}
 
 // Rows of one head that one preprocessing workgroup covers.
 constexpr int kBwdChunkRows = 256;

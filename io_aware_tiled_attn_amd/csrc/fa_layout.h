@@ -1,8 +1,10 @@
 // Index math of the kernels' LDS tiles: which global row and 16-byte chunk
 // each lane of a global -> LDS copy fetches, and where each lane's MFMA
-// operand reads land.  Plain integer functions, compiled into the kernels
-// and, on the host, into the checker that proves the copies and the reads
-// agree for every tile shape the kernels accept (tests/layout_check.hip).
+// operand reads land; and the forward kernels' workgroup order.  Plain
+// integer functions, compiled into the kernels and, on the host, into the
+// checker that proves the copies and the reads agree for every tile shape
+// the kernels accept, and that the order visits every (head, query tile)
+// once (tests/layout_check.hip).
 //
 // All tiles hold rows of `row_bytes` bytes, unpadded, as 16-byte chunks;
 // chunk c of row r is stored at chunk c ^ f(r) for a per-kernel
@@ -59,6 +61,18 @@ __host__ __device__ inline int fwd_voff(int lane, int dm) {
   const int sl = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
   const int row = 4 * g + (sl >> 2);
   return row * D + 8 * ((4 * dm + 2 * G + ((sl & 3) >> 1)) ^ FwdSwizzle<D>::v(row)) + 4 * (sl & 1);
+}
+
+// Output staging of the forward epilogue: a wave's 32 x D tile of O (bf16,
+// row = query) in LDS with K's chunk permutation.  Lane (lc, lg) writes the
+// 4 features 32 dm + 8 i + 4 lg .. + 3 of query lc (element offset below);
+// the tile is then read back 1 KB per instruction in lane order, lane i
+// taking the row and logical chunk that copy_slot(2 D, inst, i,
+// FwdSwizzle<D>::k) names, so each instruction's global stores cover
+// consecutive whole rows.
+template <int D>
+__host__ __device__ inline int fwd_ostage_off(int lc, int lg, int dm, int i) {
+  return lc * D + 8 * ((4 * dm + i) ^ FwdSwizzle<D>::k(lc)) + 4 * lg;
 }
 
 // ---------------------------------------------------------------------------
@@ -131,6 +145,55 @@ template <int D>
 __host__ __device__ inline int bwd_tr_off(int lane, int r0, int dm) {
   const int s = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
   return bwd_chunk_off<D>(r0 + 4 * g + (s >> 2), 4 * dm + 2 * G + ((s & 3) >> 1)) + 4 * (s & 1);
+}
+
+// ---------------------------------------------------------------------------
+// Forward workgroup order over num_qt query tiles x BH heads, the last query
+// tile (the heaviest under the causal mask) first.  The dispatcher hands
+// workgroup i to XCD i % 8, and each XCD has its own L2.  With hg > 0 (BH a
+// multiple of 8 hg), XCD x takes its heads x, x + 8, ... in groups of hg,
+// each group's query tiles heaviest first with the group's heads
+// interleaved.  hg is chosen (head_group_size) so that one group's tiles
+// fill what an XCD runs at once: they start together, walk the same K/V
+// tiles in step and find most of them in the XCD's L2.  With hg = 0, tiles
+// heaviest first with the head index varying fastest.
+// ---------------------------------------------------------------------------
+// Item k of XCD x's list (hg > 0): the (head, query tile) that xcd_head_groups
+// gives the k-th workgroup placed on that XCD.
+__host__ __device__ inline void xcd_item(int x, int k, int num_qt, int hg, int& bh, int& qt) {
+  const int per = hg * num_qt;
+  const int grp = k / per, r = k % per;
+  qt = num_qt - 1 - r / hg;
+  bh = x + 8 * (hg * grp + r % hg);
+}
+
+__host__ __device__ inline void xcd_head_groups(int bid, int BH, int num_qt, int hg, int& bh, int& qt) {
+  if (hg > 0) {
+    xcd_item(bid & 7, bid >> 3, num_qt, hg, bh, qt);
+  } else {
+    qt = num_qt - 1 - bid / BH;
+    bh = bid % BH;
+  }
+}
+
+// Persistent launch: W workgroups per XCD, each working through a fixed
+// list of its XCD's items (BH / 8 x num_qt of them, in xcd_item order).  In
+// round r workgroup j takes item r W + j (r even) or r W + W - 1 - j (r
+// odd), so a workgroup that drew one of a round's heavy tiles draws one of
+// the next round's light ones.  Returns -1 past the end of the list.
+__host__ __device__ inline int persistent_item(int j, int r, int W, int n_items) {
+  const int k = r * W + ((r & 1) ? W - 1 - j : j);
+  return k < n_items ? k : -1;
+}
+
+// The largest power of two g such that g heads' num_qt tiles fit in the
+// `resident` workgroups one XCD runs at once and BH is a multiple of 8 g;
+// 0 when BH is not a multiple of 8.
+__host__ __device__ inline int head_group_size(int resident, int BH, int num_qt) {
+  if (BH % 8 != 0) return 0;
+  int g = 1;
+  while (2 * g * num_qt <= resident && BH % (16 * g) == 0) g *= 2;
+  return g;
 }
 
 }  // namespace layout

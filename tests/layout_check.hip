@@ -1,7 +1,7 @@
 // Host-side check of the kernels' LDS tile index math, compiled from the
 // same header the kernels use (io_aware_tiled_attn_amd/csrc/fa_layout.h).
 // Test infrastructure: built into tests/_build/liblayout_check.so and called
-// from tests/test_layout_cpu.py; no kernel runs here.
+// from tests/test_pipeline_model.py; no kernel runs here.
 //
 // For every tile shape the kernels accept (and the wider shapes that were
 // tried and set aside), it checks
@@ -15,7 +15,13 @@
 //     cycle: 16 lanes of a 16-byte read or 32 lanes of an 8-byte read); the
 //     degree (1 = conflict-free) is reported, and for the backward's tiles,
 //     designed conflict-free, a degree above 1 counts as a violation;
-//   * the LDS the launch reserves against the 160 KB of a CU.
+//   * the LDS the launch reserves against the 160 KB of a CU;
+//   * the forward epilogue's output staging: every output element written
+//     once and read back by the lane that stores its row, each store
+//     instruction covering 1 KB of consecutive rows;
+//   * the forward's workgroup order: every (head, query tile) exactly once,
+//     each head on one XCD, each head group heaviest tile first, and group
+//     sizes that divide the XCD's heads and fit what it runs at once.
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -316,6 +322,154 @@ void check_bwd_lds(Report& rep) {
   rep.note("bwd D=%d: LDS at most %d B (dK/dV), %d B (dQ)", D, dkdv, dq);
 }
 
+// Output staging of the forward epilogue (bf16 and FP8 kernels): each lane's
+// 8-byte writes of its query's features, then the 1 KB read-back whose lanes
+// store whole consecutive rows to global memory.
+template <int D>
+void check_ostage(Report& rep) {
+  const int row_bytes = 2 * D, bytes = 32 * row_bytes;
+  std::vector<int> owner(bytes / 8, -1);   // per 8-byte slot: row * (D / 4) + 4-feature group
+  std::vector<int> wbyte(64);
+  int wdeg = 1;
+  for (int dm = 0; dm < D / 32; ++dm)
+    for (int i = 0; i < 4; ++i) {
+      for (int lane = 0; lane < 64; ++lane) {
+        const int lc = lane & 31, lg = lane >> 5;
+        const int b = 2 * fwd_ostage_off<D>(lc, lg, dm, i);
+        wbyte[lane] = b;
+        if (b < 0 || b + 8 > bytes || b % 8 != 0) {
+          rep.fail("ostage D=%d: write at byte %d outside or misaligned", D, b);
+          continue;
+        }
+        if (owner[b / 8] != -1) rep.fail("ostage D=%d: byte %d written twice", D, b);
+        owner[b / 8] = lc * (D / 4) + (32 * dm + 8 * i + 4 * lg) / 4;
+      }
+      const int d = conflict_degree(wbyte, 8);
+      if (d > wdeg) wdeg = d;
+    }
+  for (size_t k = 0; k < owner.size(); ++k)
+    if (owner[k] == -1) rep.fail("ostage D=%d: slot %zu never written", D, k);
+  std::vector<int> rbyte(64), seen(32 * (D / 8), 0);
+  int rdeg = 1;
+  for (int inst = 0; inst < bytes / 1024; ++inst) {
+    int lo = 1 << 30, hi = -1;
+    for (int lane = 0; lane < 64; ++lane) {
+      int row, chunk;
+      copy_slot(row_bytes, inst, lane, FwdSwizzle<D>::k, row, chunk);
+      const int b = inst * 1024 + 16 * lane;
+      rbyte[lane] = b;
+      if (row < 0 || row >= 32 || chunk < 0 || chunk >= D / 8) {
+        rep.fail("ostage D=%d: read inst %d lane %d names row %d chunk %d", D, inst, lane, row, chunk);
+        continue;
+      }
+      // The 16 bytes read must be features 8 chunk .. 8 chunk + 7 of `row`.
+      if (owner[b / 8] != row * (D / 4) + 2 * chunk || owner[b / 8 + 1] != row * (D / 4) + 2 * chunk + 1)
+        rep.fail("ostage D=%d: read inst %d lane %d gets slots (%d, %d), wanted row %d chunk %d", D, inst, lane,
+                 owner[b / 8], owner[b / 8 + 1], row, chunk);
+      seen[row * (D / 8) + chunk]++;
+      const int g = row * row_bytes + 16 * chunk;   // global byte offset within the wave's rows
+      lo = g < lo ? g : lo;
+      hi = g + 16 > hi ? g + 16 : hi;
+    }
+    if (lo != inst * 1024 || hi != inst * 1024 + 1024)
+      rep.fail("ostage D=%d: store inst %d covers global bytes [%d, %d), not one whole 1 KB", D, inst, lo, hi);
+    const int d = conflict_degree(rbyte, 16);
+    if (d > rdeg) rdeg = d;
+  }
+  for (size_t k = 0; k < seen.size(); ++k)
+    if (seen[k] != 1) rep.fail("ostage D=%d: (row, chunk) %zu read %d times", D, k, seen[k]);
+  if (rdeg > 1) rep.fail("ostage D=%d: read-back conflict degree %d", D, rdeg);
+  rep.note("ostage D=%d: write conflict degree %d, read-back degree %d", D, wdeg, rdeg);
+}
+
+// Workgroup order of the forward launches (xcd_head_groups with the group
+// size head_group_size picks, and every other valid size).
+void check_order(Report& rep) {
+  const int heads[] = {1, 7, 8, 12, 16, 24, 32, 64, 96, 128, 256};
+  const int tiles[] = {1, 2, 3, 5, 8, 16, 17, 32, 64, 128};
+  const int residents[] = {8, 16, 32, 64, 96};
+  int cases = 0;
+  for (int BH : heads)
+    for (int nq : tiles)
+      for (int res : residents) {
+        const int pick = head_group_size(res, BH, nq);
+        if ((pick == 0) != (BH % 8 != 0)) rep.fail("order BH=%d nq=%d res=%d: group size %d", BH, nq, res, pick);
+        if (pick > 1 && pick * nq > res) rep.fail("order BH=%d nq=%d res=%d: group of %d exceeds the XCD", BH, nq, res, pick);
+        for (int hg = 0; hg <= 32; hg = hg == 0 ? 1 : 2 * hg) {
+          if (hg > 0 && BH % (8 * hg) != 0) continue;
+          ++cases;
+          std::vector<int> seen((size_t)BH * nq, 0);
+          std::vector<int> last_qt(8 * 512, 1 << 30);   // per (XCD, group < 512): previous tile
+          for (int bid = 0; bid < BH * nq; ++bid) {
+            int bh = -1, qt = -1;
+            xcd_head_groups(bid, BH, nq, hg, bh, qt);
+            if (bh < 0 || bh >= BH || qt < 0 || qt >= nq) {
+              rep.fail("order BH=%d nq=%d hg=%d: workgroup %d -> head %d tile %d out of range", BH, nq, hg, bid, bh, qt);
+              break;
+            }
+            ++seen[(size_t)bh * nq + qt];
+            if (hg > 0) {
+              if (bh % 8 != bid % 8) rep.fail("order BH=%d nq=%d hg=%d: head %d off its XCD", BH, nq, hg, bh);
+              const int grp = (bid / 8) / (hg * nq);
+              int& prev = last_qt[(size_t)(bid % 8) * 512 + grp];
+              if (qt > prev) rep.fail("order BH=%d nq=%d hg=%d: group %d not heaviest first", BH, nq, hg, grp);
+              prev = qt;
+            }
+          }
+          for (size_t i = 0; i < seen.size(); ++i)
+            if (seen[i] != 1) {
+              rep.fail("order BH=%d nq=%d hg=%d: (head, tile) %zu visited %d times", BH, nq, hg, i, seen[i]);
+              break;
+            }
+        }
+      }
+  rep.note("order: %d (heads, tiles, group size) cases; B4 H32 N4096 at 32 resident workgroups per XCD: group of %d", cases,
+           head_group_size(32, 128, 16));
+
+  // Persistent lists: every item of an XCD's list taken by exactly one of
+  // its W workgroups; with the causal cost model (steps of 96 keys plus a
+  // fixed two per item) the busiest workgroup's total is reported.
+  int pcases = 0;
+  for (int n_items : {1, 3, 7, 8, 31, 32, 33, 64, 100, 256, 1000})
+    for (int W : {1, 2, 5, 8, 32, 64}) {
+      ++pcases;
+      std::vector<int> taken(n_items, 0);
+      for (int j = 0; j < W; ++j)
+        for (int r = 0;; ++r) {
+          const int k = persistent_item(j, r, W, n_items);
+          if (k < 0) {
+            if (r * W < n_items && persistent_item(j, r + 1, W, n_items) >= 0)
+              rep.fail("persistent n=%d W=%d: workgroup %d stops at round %d before the list ends", n_items, W, j, r);
+            break;
+          }
+          taken[k]++;
+        }
+      for (int k = 0; k < n_items; ++k)
+        if (taken[k] != 1) {
+          rep.fail("persistent n=%d W=%d: item %d taken %d times", n_items, W, k, taken[k]);
+          break;
+        }
+    }
+  {
+    const int num_qt = 16, hg = head_group_size(32, 128, num_qt), W = 32, n = 16 * num_qt;
+    double worst = 0, total = 0;
+    for (int j = 0; j < W; ++j) {
+      double c = 0;
+      for (int r = 0;; ++r) {
+        const int k = persistent_item(j, r, W, n);
+        if (k < 0) break;
+        int bh, qt;
+        xcd_item(0, k, num_qt, hg, bh, qt);
+        c += (double)(((qt + 1) * 256 + 95) / 96) + 2.0;
+      }
+      worst = c > worst ? c : worst;
+      total += c;
+    }
+    rep.note("persistent: %d list cases; B4 H32 N4096 causal, 32 workgroups per XCD: busiest %.0f of mean %.1f steps", pcases,
+             worst, total / W);
+  }
+}
+
 }  // namespace
 
 extern "C" int fa_layout_check(char* out, int out_len) {
@@ -340,6 +494,9 @@ extern "C" int fa_layout_check(char* out, int out_len) {
   check_bwd<128>(rep, 128);
   check_bwd_lds<64>(rep);
   check_bwd_lds<128>(rep);
+  check_ostage<64>(rep);
+  check_ostage<128>(rep);
+  check_order(rep);
   if (out && out_len > 0) {
     strncpy(out, rep.text.c_str(), (size_t)out_len - 1);
     out[out_len - 1] = 0;

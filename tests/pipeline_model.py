@@ -99,33 +99,49 @@ def check(groups):
 # read is of a stale buffer and unused); its vector phase is the softmax of
 # tile t + 1, and (bf16, d = 128) reads the first operands of V(t + 1) for
 # the next matrix phase.  Group 1 runs one interval behind group 0.
+#
+# The kernels copy tiles 0 and 1 before the first barrier and tile 2 right
+# after it (once both groups' first score products are issued); then, at the
+# start of its vector phase of step t, each group copies tile t + 3 into the
+# buffer of tile t and waits for everything but that copy at the phase's end.
+# `ahead` = 2 with copy_at = "matrix" is the earlier schedule (tile t + 2
+# copied at the start of the matrix phase, all copies waited for at the end
+# of the vector phase).
 # ---------------------------------------------------------------------------
-def forward_schedule(num_kt, preload_v, copy_ahead=2, bufs=3, wait_in_vector=True, waits=True):
+def forward_schedule(num_kt, preload_v, ahead=3, copy_at="vector", bufs=3, waits=True):
     groups = [Group(), Group()]
     tensor = ("K", "V")
     for gi, g in enumerate(groups):
+        def copy(t):
+            if t < num_kt:
+                g.copy("%s%d" % (tensor[gi], t % bufs), (tensor[gi], t))
+                return True
+            return False
         for t in range(min(2, num_kt)):
-            g.copy("%s%d" % (tensor[gi], t % bufs), (tensor[gi], t))
+            copy(t)
         g.wait("all")
         g.barrier()
         if num_kt > 0:
             g.read("K0", ("K", 0))                     # S of tile 0
+        if ahead == 3:
+            copy(2)
         if preload_v and num_kt > 0:
             g.read("V0", ("V", 0))
         if gi == 1:
             g.barrier()
         for t in range(num_kt):
-            if t + copy_ahead < num_kt:
-                g.copy("%s%d" % (tensor[gi], (t + copy_ahead) % bufs), (tensor[gi], t + copy_ahead))
+            copied = False
+            if copy_at == "matrix":
+                copied = copy(t + ahead)
             g.read("V%d" % (t % bufs), ("V", t))
             g.read("K%d" % ((t + 1) % bufs), ("K", t + 1) if t + 1 < num_kt else None)
-            if not wait_in_vector:
-                g.wait("all")
             g.barrier()
+            if copy_at == "vector":
+                copied = copy(t + ahead)
             if preload_v and t + 1 < num_kt:
                 g.read("V%d" % ((t + 1) % bufs), ("V", t + 1))
-            if wait_in_vector and waits:
-                g.wait("all")
+            if waits:
+                g.wait("keep_current" if copied and copy_at == "vector" else "all")
             g.barrier()
         if gi == 0:
             g.barrier()

@@ -74,10 +74,24 @@ def test_backward_schedules_are_safe(n_blk):
     assert pm.check(pm.dq_schedule(n_blk)) == []
 
 
+@pytest.mark.parametrize("preload", [False, True])
+@pytest.mark.parametrize("num_kt", range(1, 10))
+def test_earlier_forward_schedule_is_safe(num_kt, preload):
+    # Tile t + 2 copied at the start of the matrix phase of step t.
+    assert pm.check(pm.forward_schedule(num_kt, preload, ahead=2, copy_at="matrix")) == []
+
+
 def test_model_catches_planted_schedule_mistakes():
     # Two buffers for a copy two tiles ahead: the copy overwrites a tile the
     # other group still reads.
-    assert pm.check(pm.forward_schedule(6, False, bufs=2))
+    assert pm.check(pm.forward_schedule(6, False, ahead=2, copy_at="matrix", bufs=2))
+    # Three tiles ahead from the start of the matrix phase: on the first
+    # step, tile 3 lands in tile 0's buffer while the other group is still
+    # taking its first scores from it.
+    assert pm.check(pm.forward_schedule(6, False, ahead=3, copy_at="matrix"))
+    # Three tiles ahead with only three buffers is safe only from the vector
+    # phase; with two buffers it never is.
+    assert pm.check(pm.forward_schedule(6, True, bufs=2))
     # No wait for the copies: tiles are read before they are known to be in.
     assert pm.check(pm.forward_schedule(6, False, waits=False))
     # The dK/dV kernel's next block copied during the matrix phase, which
