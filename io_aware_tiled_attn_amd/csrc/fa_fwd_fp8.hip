@@ -362,6 +362,9 @@ static hipError_t launch_fp8_d(const FwdFp8Args& a) {
   auto kern = fa_fwd_fp8_kernel<D, BN, CAUSAL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   if (e != hipSuccess) return e;
+  // One workgroup per item in the head-grouped order (a persistent loop, as
+  // in the bf16 kernel, measured no faster here and costs the d = 64 build
+  // its second workgroup per CU).
   int hg = 0, wpx = 0;
   e = forward_work_layout((const void*)kern, C::kThreads, C::kLdsBytes, BH, num_qt, &hg, &wpx);
   if (e != hipSuccess) return e;
