@@ -166,6 +166,16 @@ __device__ __forceinline__ void wait_vmem_keep() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(N) that the compiler must place before any use of `addr`
+// (passed through the asm): an LDS read at an address derived from it cannot
+// move above the wait.  For reading bytes this wave's own global -> LDS
+// copies wrote, with no workgroup barrier in between.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep_before(int& addr) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(addr) : "n"(N));
+}
+
 // Work order for a launch of num_tiles x BH workgroups (tile-major work
 // items of BH heads).  The dispatcher hands workgroup i to XCD i % 8, and
 // each XCD has its own L2.  When BH is a multiple of 8, XCD x takes heads
@@ -193,7 +203,12 @@ __device__ __forceinline__ void xcd_head_major(int bid, int BH, int num_tiles, i
 // meanwhile; the wave's LDS writes and reads stay in order.
 template <int D>
 __device__ __forceinline__ void store_o_rows(const f32x16 (&oacc)[D / 32], float inv_l, __bf16* stage,
-                                             __bf16* o_head, int q0, int N, int lane) {
+                                             __bf16* o_head, int q0, int N, int lane_in) {
+  // The lane index passes through an asm so the address arithmetic below is
+  // done here, after the caller's main loop, instead of being hoisted above
+  // it and held in registers throughout.
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
   const int lc = lane & 31, lg = lane >> 5;
 #pragma unroll
   for (int dm = 0; dm < D / 32; ++dm)
@@ -203,13 +218,16 @@ __device__ __forceinline__ void store_o_rows(const f32x16 (&oacc)[D / 32], float
                        pack_bf16x2(oacc[dm][4 * i + 2] * inv_l, oacc[dm][4 * i + 3] * inv_l)};
       *(u32x2*)(stage + layout::fwd_ostage_off<D>(lc, lg, dm, i)) = w;
     }
+  // All the reads first (they overlap), then the stores of rows below N.
   constexpr int kInst = 32 * D * 2 / 1024;
+  u32x4 v[kInst];
+#pragma unroll
+  for (int j = 0; j < kInst; ++j) v[j] = *(const u32x4*)(stage + j * 512 + 8 * lane);
 #pragma unroll
   for (int j = 0; j < kInst; ++j) {
     int row, chunk;
     layout::copy_slot(2 * D, j, lane, layout::FwdSwizzle<D>::k, row, chunk);
-    const u32x4 v = *(const u32x4*)(stage + j * 512 + 8 * lane);
-    if (q0 + row < N) *(u32x4*)(o_head + (size_t)(q0 + row) * D + 8 * chunk) = v;
+    if (q0 + row < N) *(u32x4*)(o_head + (size_t)(q0 + row) * D + 8 * chunk) = v[j];
   }
 }
 

@@ -60,11 +60,13 @@ struct FwdCfg {
   static constexpr int BM = kWaves * 32;
   static constexpr int kTile = BN * D;     // bf16 elements per K or V tile (unpadded rows)
   static constexpr int kBufs = 3;          // LDS buffers per tensor
-  // LDS: K buffers 0..2 | V buffers 0..2; after the loop the same bytes
-  // stage the output rows (32 x D bf16 per wave).
+  // LDS: K buffers 0..2 | V buffers 0..2 | the Q staging slots that do not
+  // fit in the third buffers (layout::fwd_qslot) | the sparse list.  After
+  // the loop the same bytes stage the output rows (32 x D bf16 per wave).
   static constexpr int kTileBytes = 2 * kBufs * kTile * 2;
+  static constexpr int kListOff = 2 * kBufs * kTile + layout::fwd_qslot_extra<D, BN>();   // elements
   static constexpr int kStageBytes = kWaves * 32 * D * 2;
-  static constexpr int kLdsBytes = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
+  static constexpr int kLdsBytes = kListOff * 2 > kStageBytes ? kListOff * 2 : kStageBytes;
   // Each group of four waves copies one tensor; 1 KB per copy instruction.
   static constexpr int kDmaPerWave = kTile * 2 / 1024 / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
@@ -99,22 +101,44 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile,
   }
 }
 
+// This wave's 32 query rows (zeros past the head's end, through the buffer
+// descriptor) into its LDS staging slot, 1 KB of consecutive rows per
+// instruction, chunks permuted as in a K tile.
+template <int D>
+__device__ __forceinline__ void dma_q(__amdgpu_buffer_rsrc_t r, __bf16* slot, int q0, int lane) {
+#pragma unroll
+  for (int i = 0; i < 32 * D * 2 / 1024; ++i) {
+    int row, chunk;
+    layout::copy_slot(2 * D, i, lane, Swizzle<D>::k, row, chunk);
+    lds_copy16(r, (uint32_t)((q0 + row) * D + 8 * chunk) * 2u, (uint32_t)(uintptr_t)(slot + i * 512));
+  }
+}
+
 // S^T = K Q^T for one tile: BN keys x this wave's 32 queries.  The k-steps
-// run outermost so the BN/32 accumulator chains interleave.
-// koff[ks] is this lane's element offset of its A operand for k-step ks
-// (row lc, chunk 2 ks + lg, swizzled); 32-row blocks add 32 D.
-template <int D, int BN>
+// run outermost so the BN/32 accumulator chains interleave, and each
+// operand is read L products ahead of its MFMA (as in the matrix phase)
+// instead of just before it.  koff[ks] is this lane's element offset of
+// its A operand for k-step ks (row lc, chunk 2 ks + lg, swizzled); 32-row
+// blocks add 32 D.
+template <int D, int BN, int L>
 __device__ __forceinline__ void score_tile(f32x16 (&s)[BN / 32], const __bf16* Ks, const int (&koff)[D / 16],
                                           const bf16x8 (&qb)[D / 16]) {
+  constexpr int kAll = D / 16 * (BN / 32);
+  constexpr int kL = L < kAll ? L : kAll;
+  auto load = [&](int i) { return *(const bf16x8*)(Ks + koff[i / (BN / 32)] + 32 * (i % (BN / 32)) * D); };
 #pragma unroll
   for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
+  bf16x8 ring[kL];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
+  for (int i = 0; i < kL; ++i) ring[i] = load(i);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mb = 0; mb < BN / 32; ++mb) {
-      const bf16x8 a = *(const bf16x8*)(Ks + koff[ks] + 32 * mb * D);
-      s[mb] = mfma32(a, qb[ks], s[mb]);
-    }
+  for (int i = 0; i < kAll; ++i) {
+    const bf16x8 a = ring[i % kL];
+    s[i % (BN / 32)] = mfma32(a, qb[i / (BN / 32)], s[i % (BN / 32)]);
+    if (i + kL < kAll) ring[i % kL] = load(i + kL);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Keys past the end, and on the diagonal keys after the query, to -inf.
@@ -141,14 +165,23 @@ __device__ __forceinline__ float tile_exp(const f32x16 (&s)[BN / 32], bf16x8 (&p
   for (int mb = 0; mb < BN / 32; ++mb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      // Eight independent exponentials at a time, so the transcendental unit
+      // is not waiting on one score's argument after another.
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_fmaf(s[mb][8 * h + j], scale_log2, -m);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(p[j]);
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e], scale_log2, -m));
-        const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * h + 2 * e + 1], scale_log2, -m));
-        rowsum += p0 + p1;
-        w[e] = pack_bf16x2(p0, p1);
+        w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        // Pack here: left to itself the compiler moves the packs past the
+        // rescale test (they are redone when it fires) and keeps all the
+        // fp32 exponentials live until then.
+        asm volatile("" : "+v"(w[e]));
       }
+      rowsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pb[2 * mb + h] = __builtin_bit_cast(bf16x8, ((u32x4){w[0], w[1], w[2], w[3]}));
     }
   return rowsum;
@@ -337,11 +370,10 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q_wave0 = qt * C::BM + wave * 32;
   const int q_idx = q_wave0 + lc;
 
-  // Q^T as MFMA B operand: lane holds Q[q][16 ks + 8 lg .. +7] (zeros past N).
-  bf16x8 qb[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qb[ks] = __builtin_bit_cast(bf16x8, bload128(rq, (uint32_t)(q_idx * D + 16 * ks + 8 * lg) * 2u));
+  // Q first: this wave's rows into its staging slot (read back below as the
+  // MFMA B operand once the copy is in).
+  const int qslot = layout::fwd_qslot<D, BN>(wave);
+  dma_q<D>(rq, smem + qslot, q_wave0, lane);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -357,7 +389,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // Sparse: list of visited key tiles, entry = tile | keep(block 0) << 24 |
   // keep(block 1) << 25, built by wave 0 with a ballot compaction.
-  int* tlist = (int*)(smem + 2 * C::kBufs * C::kTile);   // after the tiles: [0] = count, then entries
+  int* tlist = (int*)(smem + C::kListOff);   // [0] = count, then entries
   if constexpr (SPARSE) {
     const int nb = (N + kSparseBlock - 1) / kSparseBlock;
     const uint8_t* row0 = bmask + ((size_t)bh * nb + 2 * qt) * nb;
@@ -389,7 +421,22 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // buffer j % 3.
   if (num_kt > 0) copy_tile(tile_at(0), 0);
   if (num_kt > 1) copy_tile(tile_at(1), 1);
+  // Q's copies are older than the tiles': wait for them alone, then read
+  // Q^T as the MFMA B operand (lane: Q[q][16 ks + 8 lg .. +7]) with the K
+  // tile's row reads.
+  int qaddr = qslot;
+  if (num_kt > 1) wait_vmem_keep_before<2 * C::kDmaPerWave>(qaddr);
+  else if (num_kt == 1) wait_vmem_keep_before<C::kDmaPerWave>(qaddr);
+  else wait_vmem_keep_before<0>(qaddr);
+  bf16x8 qb[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qb[ks] = *(const bf16x8*)(smem + qaddr + layout::fwd_koff<D>(lc, lg, ks));
   wait_vmem_all();
+  // The Q reads are complete (the compiler waits for them at this asm)
+  // before any wave passes the barrier and starts tile 2's copy into the
+  // third buffers, which hold some of the slots.
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qb[ks]));
   __syncthreads();
   // The third, into the still unused buffer 2; waited for at the end of the
   // first vector phase.
@@ -414,7 +461,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // S and P of the first visited tile.
   if (num_kt > 0) {
-    score_tile<D, BN>(s, kbuf(0), koff, qb);
+    score_tile<D, BN, FWD_LOOKAHEAD>(s, kbuf(0), koff, qb);
     mask_visit(0);
     softmax_first<BN>(s, pb, m_run, l_run, scale_log2);
   }
@@ -576,7 +623,7 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   // The sparse kernel keeps its list of visited key tiles (count first)
   // after the tile buffers.
   const int list_bytes = SPARSE ? ((4 * ((a.N + BN - 1) / BN + 1) + 15) & ~15) : 0;
-  const int lds = C::kTileBytes + list_bytes > C::kLdsBytes ? C::kTileBytes + list_bytes : C::kLdsBytes;
+  const int lds = C::kListOff * 2 + list_bytes > C::kLdsBytes ? C::kListOff * 2 + list_bytes : C::kLdsBytes;
   // Dynamic LDS above 64 KB must be allowed explicitly; setting the same
   // value from several threads is harmless.
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);

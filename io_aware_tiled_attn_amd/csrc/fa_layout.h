@@ -63,6 +63,26 @@ __host__ __device__ inline int fwd_voff(int lane, int dm) {
   return row * D + 8 * ((4 * dm + 2 * G + ((sl & 3) >> 1)) ^ FwdSwizzle<D>::v(row)) + 4 * (sl & 1);
 }
 
+// Q staging of the forward prologue: each wave copies its 32 query rows
+// (32 x D bf16, K's chunk permutation, so the B operand reads are the K
+// tile's row reads) into a slot of the bytes the prologue leaves unused:
+// the third K buffer, then the third V buffer (BN / 32 slots each), then
+// slots past the six tile buffers.  Element offsets, with the LDS laid out
+// as K buffers 0..2 | V buffers 0..2 of BN x D elements each.
+template <int D, int BN>
+__host__ __device__ inline int fwd_qslot(int wave) {
+  constexpr int kTile = BN * D, kSlot = 32 * D, kPerBuf = BN / 32;
+  if (wave < kPerBuf) return 2 * kTile + wave * kSlot;
+  if (wave < 2 * kPerBuf) return 5 * kTile + (wave - kPerBuf) * kSlot;
+  return 6 * kTile + (wave - 2 * kPerBuf) * kSlot;
+}
+
+// Elements past the six tile buffers that the Q slots of 8 waves need.
+template <int D, int BN>
+__host__ __device__ constexpr int fwd_qslot_extra() {
+  return (8 - 2 * (BN / 32) > 0 ? 8 - 2 * (BN / 32) : 0) * 32 * D;
+}
+
 // Output staging of the forward epilogue: a wave's 32 x D tile of O (bf16,
 // row = query) in LDS with K's chunk permutation.  Lane (lc, lg) writes the
 // 4 features 32 dm + 8 i + 4 lg .. + 3 of query lc (element offset below);

@@ -15,7 +15,9 @@
 //     cycle: 16 lanes of a 16-byte read or 32 lanes of an 8-byte read); the
 //     degree (1 = conflict-free) is reported, and for the backward's tiles,
 //     designed conflict-free, a degree above 1 counts as a violation;
-//   * the LDS the launch reserves against the 160 KB of a CU;
+//   * the forward's Q staging slots (apart from each other and from the
+//     tiles copied meanwhile) and the LDS each launch reserves against the
+//     160 KB of a CU;
 //   * the forward epilogue's output staging: every output element written
 //     once and read back by the lane that stores its row, each store
 //     instruction covering 1 KB of consecutive rows;
@@ -187,12 +189,31 @@ void check_fwd(Report& rep, bool launched) {
         const int d = conflict_degree(at, 8);
         if (d > vdeg) vdeg = d;
       }
-  // LDS of a launch: three K and three V buffers, then the sparse tile list
-  // (at most N / BN + 1 ints; N <= 65536 keeps it within 8 KB).
-  const int lds = 2 * 3 * BN * D * 2;
-  const bool fits = lds + 4 * (65536 / BN + 1) <= 160 * 1024;
+  // Q staging slots (prologue): each wave's 32 x D slot lies in the third K
+  // or V buffer or past the six buffers, apart from the other slots and
+  // from tiles 0 and 1, which are copied while Q is read.
+  const int kTile = BN * D, slot = 32 * D, qend = 6 * kTile + fwd_qslot_extra<D, BN>();
+  for (int w = 0; w < 8; ++w) {
+    const int a = fwd_qslot<D, BN>(w);
+    if (a < 0 || a + slot > qend) rep.fail("fwd bf16 D=%d BN=%d: Q slot of wave %d outside [0, %d)", D, BN, w, qend);
+    for (int u = 0; u < w; ++u) {
+      const int b = fwd_qslot<D, BN>(u);
+      if (a < b + slot && b < a + slot) rep.fail("fwd bf16 D=%d BN=%d: Q slots of waves %d and %d overlap", D, BN, u, w);
+    }
+    for (int buf : {0, 1, 3, 4})
+      if (a < (buf + 1) * kTile && buf * kTile < a + slot)
+        rep.fail("fwd bf16 D=%d BN=%d: Q slot of wave %d overlaps tile buffer %d", D, BN, w, buf);
+  }
+  // LDS of a launch: three K and three V buffers, the Q slots past them,
+  // then the sparse tile list (sparse launches use 32- and 64-key tiles; at
+  // most N / BN + 1 ints, N <= 65536 keeps it within 8 KB); at least the
+  // output staging of the epilogue (8 waves x 32 x D).
+  const int list = 128 % BN == 0 ? 4 * (65536 / BN + 1) : 0;
+  const int staged = 8 * 32 * D * 2;
+  const int lds = 2 * qend + list > staged ? 2 * qend + list : staged;
+  const bool fits = lds <= 160 * 1024;
   if (launched && !fits)
-    rep.fail("fwd bf16 D=%d BN=%d: %d bytes of tiles plus the tile list exceed 160 KB", D, BN, lds);
+    rep.fail("fwd bf16 D=%d BN=%d: %d bytes of tiles, Q slots and the tile list exceed 160 KB", D, BN, lds);
   rep.note("fwd bf16 D=%d BN=%d (%s): LDS %d B%s, K read conflict degree %d, V read degree %d", D, BN,
            launched ? "launched" : "not launched", lds, fits ? "" : " (over 160 KB)", kdeg, vdeg);
 }
