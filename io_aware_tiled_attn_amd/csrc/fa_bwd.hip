@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(512)
 fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                    const _Float16* __restrict__ dO16, _Float16* __restrict__ K16, _Float16* __restrict__ V16,
                    const float* __restrict__ rowterm, const float* __restrict__ scales, __bf16* __restrict__ dK,
-                   __bf16* __restrict__ dV, const uint8_t* __restrict__ bmask, int N, int BH, float scale,
+                   __bf16* __restrict__ dV, const uint8_t* __restrict__ bmask, int N, int BH, int wpx, float scale,
                    float scale_log2) {
   using C = BwdCfg<D>;
   static_assert(C::RES == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::BLK == 0, "sparse blocks vs tiles");
@@ -472,15 +472,33 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
   _Float16* Ks = (_Float16*)smem_raw;                              // [RES][D], permuted chunks
   _Float16* Vs = Ks + C::kResTile;
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // uniform per wave
   const int kb = wave & 3;                   // key block of this wave
   const int g = wave >> 2;                   // group
+
+  // One (128-key tile, head) item per pass: this workgroup's own (wpx = 0),
+  // or (persistent launch, wpx workgroups per XCD) its share of its XCD's
+  // head-major list.
+  const int num_tiles = (N + C::RES - 1) / C::RES;
+  const int xcd_items = BH / 8 * num_tiles;
+  for (int pass = 0;; ++pass) {
+  // The thread index enters each pass through an asm, so per-lane address
+  // arithmetic stays inside the pass rather than held across all of them.
+  int tid_v = threadIdx.x;
+  asm volatile("" : "+v"(tid_v));
+  const int tid = tid_v;
   const int gt = tid & 255;                  // thread within the group
   const int lane = tid & 63;
   const int lc = lane & 31, lg = lane >> 5;
   int kt, bh;   // key tile (small kt = most query blocks) and head
-  xcd_head_major(blockIdx.x, BH, (N + C::RES - 1) / C::RES, bh, kt);
+  if (wpx > 0) {
+    const int k = layout::persistent_item(blockIdx.x >> 3, pass, wpx, xcd_items);
+    if (k < 0) break;
+    layout::xcd_head_major_item(blockIdx.x & 7, k, num_tiles, bh, kt);
+  } else {
+    if (pass > 0) break;
+    xcd_head_major(blockIdx.x, BH, num_tiles, bh, kt);
+  }
   const BwdHead h = bwd_head<D>(Q16, K16, V16, dO16, rowterm, bh, N);
   const size_t head_off = (size_t)bh * N * D;
 
@@ -679,6 +697,10 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
     if (g == 0) finish(dk_acc, 0, dk_fac, dK + row);
     else finish(dv_acc, 1, dv_fac, dV + row);
   }
+  // The closing sum's LDS is read by every wave before the next item's
+  // copies and conversions overwrite it.
+  if (wpx > 0) __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -696,23 +718,36 @@ __global__ void __launch_bounds__(512)
 fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ K16,
                  const _Float16* __restrict__ V16, const _Float16* __restrict__ dO16,
                  const float* __restrict__ rowterm, const float* __restrict__ scales, __bf16* __restrict__ dQ,
-                 const uint8_t* __restrict__ bmask, int N, int BH, float scale, float scale_log2) {
+                 const uint8_t* __restrict__ bmask, int N, int BH, int wpx, float scale, float scale_log2) {
   using C = BwdCfg<D>;
   static_assert(C::RES == FA_SPARSE_BLOCK && FA_SPARSE_BLOCK % C::BLK == 0, "sparse blocks vs tiles");
   constexpr int KS = D / 16;
   constexpr int DM = D / 32;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int qb = wave & 3;                   // query block of this wave
   const int g = wave >> 2;                   // group
+  const int num_qt = (N + C::RES - 1) / C::RES;
+
+  // One (128-query tile, head) item per pass, as in the dK/dV kernel.
+  const int xcd_items = BH / 8 * num_qt;
+  for (int pass = 0;; ++pass) {
+  int tid_v = threadIdx.x;
+  asm volatile("" : "+v"(tid_v));
+  const int tid = tid_v;
   const int gt = tid & 255;
   const int lane = tid & 63;
   const int lc = lane & 31, lg = lane >> 5;
-  const int num_qt = (N + C::RES - 1) / C::RES;
   int tile, bh;
-  xcd_head_major(blockIdx.x, BH, num_qt, bh, tile);
+  if (wpx > 0) {
+    const int k = layout::persistent_item(blockIdx.x >> 3, pass, wpx, xcd_items);
+    if (k < 0) break;
+    layout::xcd_head_major_item(blockIdx.x & 7, k, num_qt, bh, tile);
+  } else {
+    if (pass > 0) break;
+    xcd_head_major(blockIdx.x, BH, num_qt, bh, tile);
+  }
   const int qt = num_qt - 1 - tile;          // heaviest query tiles first (causal)
   const BwdHead h = bwd_head<D>(Q16, K16, V16, dO16, rowterm, bh, N);
 
@@ -867,6 +902,10 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
     if (g == 0) finish(0);
     else finish(kHalf);
   }
+  // The closing sum's LDS is read by every wave before the next item's
+  // copies overwrite it.
+  if (wpx > 0) __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -902,10 +941,13 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     auto kern = fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE>;
     if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL(kern, dim3(num_tiles * BH), dim3(C::kThreads), lds, a.stream, q16, (const __bf16*)a.k,
+    int wpx = 0;
+    if ((e = persistent_width((const void*)kern, C::kThreads, lds, BH, num_tiles, &wpx)) != hipSuccess) return e;
+    const int grid = wpx > 0 ? 8 * wpx : num_tiles * BH;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, a.stream, q16, (const __bf16*)a.k,
                        (const __bf16*)a.v, do16, (_Float16*)a.k16, (_Float16*)a.v16,
                        (const float*)a.rowterm, (const float*)a.scales, (__bf16*)a.dk, (__bf16*)a.dv,
-                       (const uint8_t*)a.bmask, a.N, BH, a.scale, a.scale * kLog2e);
+                       (const uint8_t*)a.bmask, a.N, BH, wpx, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.phases & FA_BWD_FINALIZE) {
@@ -913,9 +955,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, dq_lds)) !=
         hipSuccess)
       return e;
-    hipLaunchKernelGGL(kern, dim3(num_tiles * BH), dim3(C::kThreads), dq_lds, a.stream, q16, k16, v16, do16,
+    int wpx = 0;
+    if ((e = persistent_width((const void*)kern, C::kThreads, dq_lds, BH, num_tiles, &wpx)) != hipSuccess) return e;
+    const int grid = wpx > 0 ? 8 * wpx : num_tiles * BH;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), dq_lds, a.stream, q16, k16, v16, do16,
                        (const float*)a.rowterm, (const float*)a.scales, (__bf16*)a.dq, (const uint8_t*)a.bmask,
-                       a.N, BH, a.scale, a.scale * kLog2e);
+                       a.N, BH, wpx, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return e;

@@ -186,9 +186,7 @@ __device__ __forceinline__ void wait_vmem_keep_before(int& addr) {
 // fastest.
 __device__ __forceinline__ void xcd_head_major(int bid, int BH, int num_tiles, int& bh, int& tile) {
   if ((BH & 7) == 0) {
-    const int j = bid >> 3;
-    tile = j % num_tiles;
-    bh = (j / num_tiles) * 8 + (bid & 7);
+    layout::xcd_head_major_item(bid & 7, bid >> 3, num_tiles, bh, tile);
   } else {
     tile = bid / BH;
     bh = bid % BH;

@@ -61,6 +61,23 @@ inline hipError_t forward_work_layout(const void* kern, int threads, int lds, in
   return hipSuccess;
 }
 
+// Workgroups per XCD of a persistent launch of `kern` over BH heads x
+// tiles_per_head items (layout::persistent_item over each XCD's
+// head-major list): as many as one XCD runs at once, at most its items; 0
+// (one workgroup per item) when BH is not a multiple of 8.
+inline hipError_t persistent_width(const void* kern, int threads, int lds, int BH, int tiles_per_head, int* wpx) {
+  *wpx = 0;
+  if (BH % 8 != 0) return hipSuccess;
+  int occ = 0, dev = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, (size_t)lds);
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int resident = occ * cus / 8, items = BH / 8 * tiles_per_head;
+  *wpx = resident < 1 ? 0 : (resident < items ? resident : items);
+  return hipSuccess;
+}
+
 // Rows of one head that one preprocessing workgroup covers.
 constexpr int kBwdChunkRows = 256;
 

@@ -196,6 +196,14 @@ __host__ __device__ inline void xcd_head_groups(int bid, int BH, int num_qt, int
   }
 }
 
+// Item k of XCD x in the backward kernels' head-major order: the XCD's heads
+// x, x + 8, ... one after another, all num_tiles tiles of a head before the
+// next, tile 0 first.
+__host__ __device__ inline void xcd_head_major_item(int x, int k, int num_tiles, int& bh, int& tile) {
+  tile = k % num_tiles;
+  bh = (k / num_tiles) * 8 + x;
+}
+
 // Persistent launch: W workgroups per XCD, each working through a fixed
 // list of its XCD's items (BH / 8 x num_qt of them, in xcd_item order).  In
 // round r workgroup j takes item r W + j (r even) or r W + W - 1 - j (r
