@@ -648,15 +648,23 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
   // The fp16 K, V rows of the tile (rows below N) on to the workspace for
   // the dQ kernel; the closing sum below reuses this LDS.
   {
+    // All the LDS reads first (they overlap), then the stores.
     constexpr int kChunks = C::RES * D / 8 / C::kThreads;
+    u32x4 kv[kChunks], vv[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + i * C::kThreads, row = c / (D / 8), ch = c % (D / 8);
+      const int lo = bwd_chunk_off<D>(row, ch);
+      kv[i] = *(const u32x4*)(Ks + lo);
+      vv[i] = *(const u32x4*)(Vs + lo);
+    }
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int c = tid + i * C::kThreads, row = c / (D / 8), ch = c % (D / 8);
       if (k0 + row < N) {
-        const int lo = bwd_chunk_off<D>(row, ch);
         const size_t go = head_off + (size_t)(k0 + row) * D + 8 * ch;
-        *(u32x4*)(K16 + go) = *(const u32x4*)(Ks + lo);
-        *(u32x4*)(V16 + go) = *(const u32x4*)(Vs + lo);
+        *(u32x4*)(K16 + go) = kv[i];
+        *(u32x4*)(V16 + go) = vv[i];
       }
     }
   }
@@ -678,24 +686,28 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
       *red_at(t, c) = (f32x4){a[c / 4][4 * (c % 4)], a[c / 4][4 * (c % 4) + 1], a[c / 4][4 * (c % 4) + 2],
                               a[c / 4][4 * (c % 4) + 3]};
   };
-  auto finish = [&](const f32x16 (&a)[DM], int t, float fac, __bf16* out) {
+  auto add_partner = [&](f32x16 (&a)[DM], int t) {
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
       const f32x4 b = *red_at(t, c);
       const int dm = c / 4, r0 = 4 * (c % 4);
-      // Registers r0 .. r0 + 3 of block dm hold features 32 dm + 8 (r0 / 4) + 4 lg + 0..3.
-      *(u32x2*)(out + 32 * dm + 8 * (c % 4) + 4 * lg) =
-          (u32x2){pack_bf16x2((a[dm][r0] + b[0]) * fac, (a[dm][r0 + 1] + b[1]) * fac),
-                  pack_bf16x2((a[dm][r0 + 2] + b[2]) * fac, (a[dm][r0 + 3] + b[3]) * fac)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[dm][r0 + e] += b[e];
     }
   };
   if (g == 0) put(dv_acc, 1);
   else put(dk_acc, 0);
   __syncthreads();
-  if (key_ok) {
-    const size_t row = ((size_t)bh * N + key) * D;
-    if (g == 0) finish(dk_acc, 0, dk_fac, dK + row);
-    else finish(dv_acc, 1, dv_fac, dV + row);
+  if (g == 0) add_partner(dk_acc, 0);
+  else add_partner(dv_acc, 1);
+  // Every partial is read before the LDS stages the finished rows: this
+  // wave's 32 keys (rows kw0 .. kw0 + 31) of its tensor, written as whole
+  // rows.
+  __syncthreads();
+  {
+    __bf16* stage = (__bf16*)smem_raw + wave * 32 * D;
+    if (g == 0) store_o_rows<D>(dk_acc, dk_fac, stage, dK + head_off, kw0, N, lane);
+    else store_o_rows<D>(dv_acc, dv_fac, stage, dV + head_off, kw0, N, lane);
   }
   // The closing sum's LDS is read by every wave before the next item's
   // copies and conversions overwrite it.
@@ -884,23 +896,30 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
                            dq_acc[c / 4][4 * (c % 4) + 3]};
     }
   };
-  auto finish = [&](int c0) {
-    __bf16* out = dQ + ((size_t)bh * N + q) * D;
+  auto add_partner = [&](int c0) {
 #pragma unroll
     for (int j = 0; j < kHalf; ++j) {
       const int c = c0 + j, dm = c / 4, r0 = 4 * (c % 4);
       const f32x4 b = *red_at(c);
-      *(u32x2*)(out + 32 * dm + 8 * (c % 4) + 4 * lg) =
-          (u32x2){pack_bf16x2((dq_acc[dm][r0] + b[0]) * dq_fac, (dq_acc[dm][r0 + 1] + b[1]) * dq_fac),
-                  pack_bf16x2((dq_acc[dm][r0 + 2] + b[2]) * dq_fac, (dq_acc[dm][r0 + 3] + b[3]) * dq_fac)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dq_acc[dm][r0 + e] += b[e];
     }
   };
   if (g == 0) put(kHalf);
   else put(0);
   __syncthreads();
-  if (q < N) {
-    if (g == 0) finish(0);
-    else finish(kHalf);
+  if (g == 0) add_partner(0);
+  else add_partner(kHalf);
+  // Every partial is read before the LDS stages the finished rows: this
+  // wave's half (D / 2 columns) of its 32 query rows, staged in its own
+  // LDS and written as whole half rows.
+  __syncthreads();
+  {
+    __bf16* stage = (__bf16*)smem_raw + wave * 32 * (D / 2);
+    __bf16* out = dQ + (size_t)bh * N * D + g * (D / 2);
+    if (g == 0) stage_rows<D, D / 2>(dq_acc, dq_fac, stage, lane, 0);
+    else stage_rows<D, D / 2>(dq_acc, dq_fac, stage, lane, DM / 2);
+    write_staged_rows<D / 2>(stage, out, D, qw0, N, lane);
   }
   // The closing sum's LDS is read by every wave before the next item's
   // copies overwrite it.

@@ -193,40 +193,61 @@ __device__ __forceinline__ void xcd_head_major(int bid, int BH, int num_tiles, i
   }
 }
 
-// Forward epilogue: this wave's 32 output rows (queries q0 .. q0 + 31, the
-// O^T accumulators times inv_l rounded to bf16) staged through the wave's
-// own 64 D bytes of LDS at `stage` and written as whole rows, 1 KB of
-// consecutive rows per store instruction (instead of 16 bytes in each of
-// 32 rows).  Rows at or past N are skipped.  No other wave may use `stage`
-// meanwhile; the wave's LDS writes and reads stay in order.
-template <int D>
-__device__ __forceinline__ void store_o_rows(const f32x16 (&oacc)[D / 32], float inv_l, __bf16* stage,
-                                             __bf16* o_head, int q0, int N, int lane_in) {
-  // The lane index passes through an asm so the address arithmetic below is
-  // done here, after the caller's main loop, instead of being hoisted above
-  // it and held in registers throughout.
+// Row-wise output of a 32 x D tile held as transposed-product accumulators
+// (lane l: row l % 32; register r of 32-column block dm: columns
+// 32 dm + 8 (r / 4) + 4 (l / 32) + r % 4), rounded to bf16 after a multiply
+// by `fac`, through LDS, so that each global store instruction writes 1 KB
+// of whole row segments (instead of 16 bytes in each of 32 rows).
+// stage_rows puts the W columns of blocks dm0 .. dm0 + W / 32 - 1 into the
+// 64 W bytes at `stage` (layout::fwd_ostage_off for a W-column tile);
+// write_staged_rows reads them back 1 KB at a time and stores the rows
+// q0 .. q0 + 31 below N at out + row * pitch (W columns each).  A wave's own
+// LDS writes and reads stay in order, so a wave that stages and writes its
+// own tile needs no barrier in between.  The lane index passes through an
+// asm so the address arithmetic is done here, after the caller's main loop,
+// instead of being hoisted above it and held in registers throughout.
+template <int D, int W = D>
+__device__ __forceinline__ void stage_rows(const f32x16 (&acc)[D / 32], float fac, __bf16* stage, int lane_in,
+                                           int dm0 = 0) {
+  static_assert(W % 32 == 0 && W <= D, "staged width");
   int lane = lane_in;
   asm volatile("" : "+v"(lane));
   const int lc = lane & 31, lg = lane >> 5;
 #pragma unroll
-  for (int dm = 0; dm < D / 32; ++dm)
+  for (int b = 0; b < W / 32; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x2 w = {pack_bf16x2(oacc[dm][4 * i + 0] * inv_l, oacc[dm][4 * i + 1] * inv_l),
-                       pack_bf16x2(oacc[dm][4 * i + 2] * inv_l, oacc[dm][4 * i + 3] * inv_l)};
-      *(u32x2*)(stage + layout::fwd_ostage_off<D>(lc, lg, dm, i)) = w;
+      const f32x16& a = acc[dm0 + b];
+      const u32x2 w = {pack_bf16x2(a[4 * i + 0] * fac, a[4 * i + 1] * fac),
+                       pack_bf16x2(a[4 * i + 2] * fac, a[4 * i + 3] * fac)};
+      *(u32x2*)(stage + layout::fwd_ostage_off<W>(lc, lg, b, i)) = w;
     }
+}
+
+template <int W>
+__device__ __forceinline__ void write_staged_rows(const __bf16* stage, __bf16* out, int pitch, int q0, int N,
+                                                  int lane_in) {
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
   // All the reads first (they overlap), then the stores of rows below N.
-  constexpr int kInst = 32 * D * 2 / 1024;
+  constexpr int kInst = 32 * W * 2 / 1024;
   u32x4 v[kInst];
 #pragma unroll
   for (int j = 0; j < kInst; ++j) v[j] = *(const u32x4*)(stage + j * 512 + 8 * lane);
 #pragma unroll
   for (int j = 0; j < kInst; ++j) {
     int row, chunk;
-    layout::copy_slot(2 * D, j, lane, layout::FwdSwizzle<D>::k, row, chunk);
-    if (q0 + row < N) *(u32x4*)(o_head + (size_t)(q0 + row) * D + 8 * chunk) = v[j];
+    layout::copy_slot(2 * W, j, lane, layout::FwdSwizzle<W>::k, row, chunk);
+    if (q0 + row < N) *(u32x4*)(out + (size_t)(q0 + row) * pitch + 8 * chunk) = v[j];
   }
+}
+
+// A wave's whole tile: stage all its blocks into its own LDS, then write.
+template <int D>
+__device__ __forceinline__ void store_o_rows(const f32x16 (&acc)[D / 32], float fac, __bf16* stage, __bf16* out,
+                                             int q0, int N, int lane) {
+  stage_rows<D>(acc, fac, stage, lane);
+  write_staged_rows<D>(stage, out, D, q0, N, lane);
 }
 
 }  // namespace fa

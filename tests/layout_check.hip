@@ -515,6 +515,7 @@ extern "C" int fa_layout_check(char* out, int out_len) {
   check_bwd<128>(rep, 128);
   check_bwd_lds<64>(rep);
   check_bwd_lds<128>(rep);
+  check_ostage<32>(rep);
   check_ostage<64>(rep);
   check_ostage<128>(rep);
   check_order(rep);
