@@ -257,7 +257,10 @@ struct BwdCfg {
   static constexpr int kLdsTotal = kLdsBytes > kRedBytes ? kLdsBytes : kRedBytes;
   // The dQ kernel's blocks are K and V only, three buffers per group.
   static constexpr int kDqStageBytes = 2 * kBlkTile * 2;
-  static constexpr int kDqLdsTotal = 6 * kDqStageBytes > kRedBytes / 2 ? 6 * kDqStageBytes : kRedBytes / 2;
+  // Six block buffers and (prologue) the Q/dO slots past them
+  // (layout::bwd_dq_qslot), or the closing sum.
+  static constexpr int kDqLdsTotal = 8 * kDqStageBytes > kRedBytes / 2 ? 8 * kDqStageBytes : kRedBytes / 2;
+  static_assert(kDqLdsTotal + 4 * (65536 / BLK + 1) <= 160 * 1024, "dQ LDS budget (with a sparse block list)");
   static_assert(kLdsTotal + 4 * (65536 / BLK + 1) <= 160 * 1024, "LDS budget (with a sparse block list)");
   static_assert(kResBytes % 1024 == 0 && kStageBytes % 256 == 0 && kBlkTile * 2 % 1024 == 0, "tile alignment");
 };
@@ -770,15 +773,10 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
   const float c2 = scale_log2 / (sq * sk);
   const float dq_fac = scale / (sk * sg * sv);
 
-  // Q^T and dO^T as B operands: lane holds 8 features of its query's row
-  // (zeros past N).
-  f16x8 qbf[KS], gbf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t off = (uint32_t)(q * D + 16 * ks + 8 * lg) * 2u;
-    qbf[ks] = __builtin_bit_cast(f16x8, bload128(h.q, off));
-    gbf[ks] = __builtin_bit_cast(f16x8, bload128(h.g, off));
-  }
+  // Q (waves 0-3) or dO (waves 4-7) rows of this wave's query block into
+  // its LDS slot, 1 KB of consecutive rows per copy (zeros past N); read
+  // back below as the B operands.
+  dma_rows<D, C::BLK, 1>(g == 0 ? h.q : h.g, (_Float16*)(smem_raw + layout::bwd_dq_qslot<D>(wave)), qw0, 0, lane);
   // Start values of this lane's S^T and dP^T accumulators: -LSE log2 e / c2
   // (-inf past N, so P = 0 there) and -D in the scaled dP's units; then
   // P^T = exp2(c2 S^T) and dS^T = P^T dP^T.
@@ -825,18 +823,33 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) dsw[i] = 0u;
 
-  // The group's first two blocks into buffers 0 and 1; zeros into the
-  // buffers a round reads before any block was copied there (buffer 2 in
-  // round 0's gradient products, buffers 0 and 1 when the group has no such
-  // block): finite operands for the products a group runs without a block.
+  // The group's first two blocks into buffers 0 and 1; zeros into those of
+  // them the group has no block for.  The products a round runs without a
+  // block need finite operands: buffers 0 and 1 then hold zeros, buffer 2
+  // (read by round 0's gradient product, whose dS is zero) the Q slots.
   if (valid(0)) stage(0, 0);
   if (valid(1)) stage(1, 1);
-  for (int b = 0; b < 3; ++b)
-    if (b == 2 || !valid(b))
+  for (int b = 0; b < 2; ++b)
+    if (!valid(b))
       for (int i = gt; i < C::kDqStageBytes / 16; i += 256)
         ((u32x4*)(gstage + b * C::kDqStageBytes))[i] = (u32x4){0u, 0u, 0u, 0u};
   wait_vmem_all();
   __syncthreads();
+  // Q^T and dO^T as B operands: lane holds 8 features of its query's row.
+  // The reads complete here (the asm uses them), before any wave passes a
+  // barrier after which block 2's copy may land on the slots in buffer 2.
+  f16x8 qbf[KS], gbf[KS];
+  {
+    const _Float16* qs = (const _Float16*)(smem_raw + layout::bwd_dq_qslot<D>(qb));
+    const _Float16* gs = (const _Float16*)(smem_raw + layout::bwd_dq_qslot<D>(4 + qb));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qbf[ks] = *(const f16x8*)(qs + bwd_chunk_off<D>(lc, 2 * ks + lg));
+      gbf[ks] = *(const f16x8*)(gs + bwd_chunk_off<D>(lc, 2 * ks + lg));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qbf[ks]), "+v"(gbf[ks]));
+  }
   if (g == 1) __syncthreads();
   int cb = 0;   // r % 3
   for (int r = 0; r <= R; ++r) {

@@ -167,6 +167,17 @@ __host__ __device__ inline int bwd_tr_off(int lane, int r0, int dm) {
   return bwd_chunk_off<D>(r0 + 4 * g + (s >> 2), 4 * dm + 2 * G + ((s & 3) >> 1)) + 4 * (s & 1);
 }
 
+// Q and dO staging of the dQ kernel's prologue: slot w (byte offset) holds
+// the 32 x D fp16 rows that wave w copies (waves 0-3 Q, waves 4-7 dO of
+// query block w % 4), in the bwd_swz layout.  The LDS holds each group's
+// three block buffers of S = 128 D bytes (K rows, then V rows) at
+// g 3 S + b S; slots 0-3 fill the third buffers of both groups, slots 4-7
+// follow the six buffers.
+template <int D>
+__host__ __device__ constexpr int bwd_dq_qslot(int w) {
+  return w < 4 ? (w >> 1) * 3 * (128 * D) + 2 * (128 * D) + (w & 1) * (64 * D) : 6 * (128 * D) + (w - 4) * (64 * D);
+}
+
 // ---------------------------------------------------------------------------
 // Forward workgroup order over num_qt query tiles x BH heads, the last query
 // tile (the heaviest under the causal mask) first.  The dispatcher hands

@@ -331,13 +331,14 @@ void check_bwd(Report& rep, int rows) {
 
 // LDS the backward launches reserve: dK/dV kernel (resident K, V; two
 // buffers of Q, dO and row terms per group; or the closing sum) and dQ
-// kernel (three K, V buffers per group; or its closing sum), each plus the
-// sparse block list (at most N / 32 + 1 ints, N <= 65536).
+// kernel (three K, V buffers per group and the Q/dO slots past them; or its
+// closing sum), each plus the sparse block list (at most N / 32 + 1 ints,
+// N <= 65536).
 template <int D>
 void check_bwd_lds(Report& rep) {
   const int res = 2 * 128 * D * 2, stage = 2 * 32 * D * 2 + 32 * 8, red = D * 4 * 64 * 4;
   const int dkdv = (res + 4 * stage > red ? res + 4 * stage : red) + 4 * (65536 / 32 + 1);
-  const int dq = (6 * 2 * 32 * D * 2 > red / 2 ? 6 * 2 * 32 * D * 2 : red / 2) + 4 * (65536 / 32 + 1);
+  const int dq = (8 * 2 * 32 * D * 2 > red / 2 ? 8 * 2 * 32 * D * 2 : red / 2) + 4 * (65536 / 32 + 1);
   if (dkdv > 160 * 1024) rep.fail("bwd D=%d: dK/dV kernel LDS %d B exceeds 160 KB", D, dkdv);
   if (dq > 160 * 1024) rep.fail("bwd D=%d: dQ kernel LDS %d B exceeds 160 KB", D, dq);
   rep.note("bwd D=%d: LDS at most %d B (dK/dV), %d B (dQ)", D, dkdv, dq);
@@ -491,6 +492,39 @@ void check_order(Report& rep) {
   }
 }
 
+// The dQ kernel's Q/dO slots: apart from each other and from each group's
+// first two block buffers (copied while the slots are read), slots 0-3
+// exactly covering the third buffers of both groups (round 0 reads them as
+// finite operands of a product with zero dS), all within 8 S bytes.
+template <int D>
+void check_dq_slots(Report& rep) {
+  const int S = 128 * D, slot = 64 * D;
+  std::vector<int> cover(8 * S / 16, 0);
+  for (int w = 0; w < 8; ++w) {
+    const int a = bwd_dq_qslot<D>(w);
+    if (a < 0 || a + slot > 8 * S || a % 1024 != 0)
+      rep.fail("dq slots D=%d: slot %d at %d outside or misaligned", D, w, a);
+    for (int g = 0; g < 2; ++g)
+      for (int b = 0; b < 2; ++b) {
+        const int lo = g * 3 * S + b * S;
+        if (a < lo + S && lo < a + slot) rep.fail("dq slots D=%d: slot %d overlaps group %d buffer %d", D, w, g, b);
+      }
+    for (int x = a / 16; x < (a + slot) / 16 && x < (int)cover.size(); ++x) cover[x]++;
+  }
+  for (size_t x = 0; x < cover.size(); ++x)
+    if (cover[x] > 1) {
+      rep.fail("dq slots D=%d: byte %zu in two slots", D, 16 * x);
+      break;
+    }
+  for (int g = 0; g < 2; ++g)
+    for (int x = (g * 3 * S + 2 * S) / 16; x < (g * 3 * S + 3 * S) / 16; ++x)
+      if (cover[x] != 1) {
+        rep.fail("dq slots D=%d: group %d buffer 2 byte %d not covered by a slot", D, g, 16 * x);
+        break;
+      }
+  rep.note("dq slots D=%d: 8 slots of %d B, third buffers covered, LDS %d B before the block list", D, slot, 8 * S);
+}
+
 }  // namespace
 
 extern "C" int fa_layout_check(char* out, int out_len) {
@@ -518,6 +552,8 @@ extern "C" int fa_layout_check(char* out, int out_len) {
   check_ostage<32>(rep);
   check_ostage<64>(rep);
   check_ostage<128>(rep);
+  check_dq_slots<64>(rep);
+  check_dq_slots<128>(rep);
   check_order(rep);
   if (out && out_len > 0) {
     strncpy(out, rep.text.c_str(), (size_t)out_len - 1);
