@@ -973,8 +973,13 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     auto kern = fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE>;
     if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
       return e;
+    // Persistent for dense masks; a block mask can give its tiles any mix of
+    // costs (a global column's tile visits every query block), which the
+    // fixed lists would not balance, so sparse launches keep one workgroup
+    // per tile and the hardware's dispatch.
     int wpx = 0;
-    if ((e = persistent_width((const void*)kern, C::kThreads, lds, BH, num_tiles, &wpx)) != hipSuccess) return e;
+    if (!SPARSE && (e = persistent_width((const void*)kern, C::kThreads, lds, BH, num_tiles, &wpx)) != hipSuccess)
+      return e;
     const int grid = wpx > 0 ? 8 * wpx : num_tiles * BH;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, a.stream, q16, (const __bf16*)a.k,
                        (const __bf16*)a.v, do16, (_Float16*)a.k16, (_Float16*)a.v16,
@@ -987,8 +992,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, dq_lds)) !=
         hipSuccess)
       return e;
-    int wpx = 0;
-    if ((e = persistent_width((const void*)kern, C::kThreads, dq_lds, BH, num_tiles, &wpx)) != hipSuccess) return e;
+    int wpx = 0;   // persistent for dense masks only, as above
+    if (!SPARSE && (e = persistent_width((const void*)kern, C::kThreads, dq_lds, BH, num_tiles, &wpx)) != hipSuccess)
+      return e;
     const int grid = wpx > 0 ? 8 * wpx : num_tiles * BH;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), dq_lds, a.stream, q16, k16, v16, do16,
                        (const float*)a.rowterm, (const float*)a.scales, (__bf16*)a.dq, (const uint8_t*)a.bmask,

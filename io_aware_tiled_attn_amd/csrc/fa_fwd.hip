@@ -631,6 +631,10 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   int hg = 0, wpx = 0;
   e = forward_work_layout((const void*)kern, C::kThreads, lds, BH, num_qt, &hg, &wpx);
   if (e != hipSuccess) return e;
+  // A block mask can give the items any mix of costs, which the fixed
+  // persistent lists would not balance: sparse launches keep one workgroup
+  // per item and the hardware's dispatch.
+  if (SPARSE) wpx = 0;
   const int grid = wpx > 0 ? 8 * wpx : num_qt * BH;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (__bf16*)a.o, a.lse, (const uint8_t*)a.bmask, a.N, BH, num_qt, hg, wpx,
