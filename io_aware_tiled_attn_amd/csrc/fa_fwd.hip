@@ -268,16 +268,21 @@ __device__ __forceinline__ void matrix_preload(bf16x8 (&ring)[L], const __bf16* 
   for (int i = 0; i < L; ++i) ring[i] = matrix_load<D, BN>(i, Vs, voff, Ks, koff);
 }
 
-template <int D, int BN, int L, bool PRELOADED>
+// SCORES = false (the last step of an item): the P V products only (when
+// the ring is deeper than they are, its in-phase preload also reads score
+// operands of a stale K buffer, which go unused).
+template <int D, int BN, int L, bool PRELOADED, bool SCORES = true>
 __device__ __forceinline__ void matrix_phase(bf16x8 (&ring)[L], f32x16 (&oacc)[D / 32], const bf16x8 (&pb)[BN / 16],
                                              const __bf16* Vs, const int (&voff)[D / 32], f32x16 (&s)[BN / 32],
                                              const __bf16* Ks, const int (&koff)[D / 16],
                                              const bf16x8 (&qb)[D / 16]) {
   constexpr int kPv = BN / 16 * (D / 32);   // O += P V products
   constexpr int kS = D / 16 * (BN / 32);    // S = K Q^T products
-  constexpr int kAll = kPv + kS;
+  constexpr int kAll = kPv + (SCORES ? kS : 0);
+  if constexpr (SCORES) {
 #pragma unroll
-  for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
+    for (int mb = 0; mb < BN / 32; ++mb) s[mb] = (f32x16){};
+  }
   // The matrix wave takes issue priority over the SIMD's other wave (in its
   // vector phase), so MFMAs are not held back behind its exponentials.
   __builtin_amdgcn_s_setprio(1);
@@ -489,30 +494,35 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (group == 1) __syncthreads();
 
   int b_cur = 0;   // t % 3
-  for (int t = 0; t < num_kt; ++t) {
+  for (int t = 0; t + 1 < num_kt; ++t) {
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;    // (t + 1) % 3
     const int b_after = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
     // wave runs the same instruction stream on every step: on causal tiles
     // wholly above a wave's queries its P is all zero (the tile is masked
-    // like any other), and on the last step the score product reads a stale
-    // buffer and its result is not used.
+    // like any other).
     matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1).
     const bool copy_next = t + 3 < num_kt;
     if (copy_next) copy_tile(tile_at(t + 3), b_cur);
-    if (t + 1 < num_kt) {
-      mask_visit(t + 1);
-      softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
-      // V(t+1)'s copy was waited for at the end of the previous step, so the
-      // barrier before this phase published it.
-      if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(b_next), voff, kbuf(b_after), koff);
-    }
+    mask_visit(t + 1);
+    softmax_step<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
+    // V(t+1)'s copy was waited for at the end of the previous step, so the
+    // barrier before this phase published it.
+    if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(b_next), voff, kbuf(b_after), koff);
     if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
     else wait_vmem_all();
     __syncthreads();
     b_cur = b_next;
+  }
+  // The last step (outside the loop, so the loop's code stays one stream):
+  // O += P V only, there being no next tile; the same two barriers.
+  if (num_kt > 0) {
+    matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload, false>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_cur), koff, qb);
+    __syncthreads();
+    wait_vmem_all();
+    __syncthreads();
   }
   if (group == 0) __syncthreads();
 
