@@ -26,7 +26,8 @@
 //   1. bwd_prep: per 256-row chunk of a head, D_i = <dO_i, O_i> in fp32 from
 //      the bf16 O, and the chunk's largest |Q|, |dO|, |K|, |V|.
 //   2. bwd_convert: the head's factors, the scaled fp16 copies of Q and dO,
-//      and per row LSE log2 e and D in the scaled units.
+//      and per row the start values of the S and dP accumulators,
+//      -LSE log2 e / c2 and -D in the scaled units.
 //   3. bwd_dkdv: key-major, one workgroup per 128-key tile; writes dK, dV,
 //      and the scaled fp16 copies of its K and V rows.
 //   4. bwd_dq: query-major, one workgroup per 128-query tile; writes dQ.
@@ -141,16 +142,19 @@ fa_bwd_prep_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, 
 // ---------------------------------------------------------------------------
 // 2. Per 256-row chunk of a head: the head's factors (from all its chunk
 //    maxima), the chunk's rows of Q and dO times their factors as fp16,
-//    and its row terms (LSE log2 e, +inf for a row that saw no key, so that
-//    P = 0 there; D times the dO and V factors).  The chunk-0 workgroup of
-//    each head records the factors.
+//    and its row terms, in two planes of N floats per head: the start value
+//    of the row's S accumulator, -LSE log2 e / c2 with c2 the exponent's
+//    multiplier of the scaled S (-inf for a row that saw no key, so that
+//    P = exp2(c2 S) = 0 there), and of its dP accumulator, -D times the dO
+//    and V factors (so that dS = P dP).  The chunk-0 workgroup of each head
+//    records the factors.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
 fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
                       const float* __restrict__ delta, const float* __restrict__ part, float* __restrict__ scales,
                       float* __restrict__ rowterm, _Float16* __restrict__ Q16, _Float16* __restrict__ dO16, int N,
-                      int nch) {
+                      int nch, float scale_log2) {
   __shared__ float red[4];
   const int bh = blockIdx.x / nch, ch = blockIdx.x % nch;
   const int tid = threadIdx.x;
@@ -170,8 +174,10 @@ fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ d
   const size_t rbase = (size_t)bh * N + row0;
   if (tid < rows) {
     const float l = LSE[rbase + tid];
-    *(f32x2*)(rowterm + 2 * (rbase + tid)) =
-        (f32x2){l == -INFINITY ? INFINITY : l * kLog2e, delta[rbase + tid] * (f[1] * f[3])};
+    const float c2 = scale_log2 / (f[0] * f[2]);
+    float* plane = rowterm + (size_t)2 * bh * N;
+    plane[row0 + tid] = l == -INFINITY ? -INFINITY : -(l * kLog2e) / c2;
+    plane[N + row0 + tid] = -(delta[rbase + tid] * (f[1] * f[3]));
   }
   const __bf16* src[2] = {Q, dO};
   _Float16* dst[2] = {Q16, dO16};
@@ -265,10 +271,11 @@ struct BwdCfg {
   static_assert(kResBytes % 1024 == 0 && kStageBytes % 256 == 0 && kBlkTile * 2 % 1024 == 0, "tile alignment");
 };
 
-// Per-head buffer descriptors over the fp16 copies and the row terms: rows
-// past N read as zero.
+// Per-head buffer descriptors over the fp16 copies and the two row-term
+// planes (rt0: S start values, rt1: dP start values): rows past N read as
+// zero.
 struct BwdHead {
-  __amdgpu_buffer_rsrc_t q, k, v, g, rt;
+  __amdgpu_buffer_rsrc_t q, k, v, g, rt0, rt1;
 };
 
 template <int D>
@@ -281,7 +288,8 @@ __device__ __forceinline__ BwdHead bwd_head(const _Float16* Q16, const _Float16*
   h.k = make_rsrc(K16 + head_off, head_bytes);
   h.v = make_rsrc(V16 + head_off, head_bytes);
   h.g = make_rsrc(dO16 + head_off, head_bytes);
-  h.rt = make_rsrc(rowterm + (size_t)2 * bh * N, (uint32_t)N * 8u);
+  h.rt0 = make_rsrc(rowterm + (size_t)2 * bh * N, (uint32_t)N * 4u);
+  h.rt1 = make_rsrc(rowterm + (size_t)2 * bh * N + N, (uint32_t)N * 4u);
   return h;
 }
 
@@ -352,7 +360,8 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
                                                   const uint32_t (&pw)[8], const uint32_t (&dsw)[8], f32x16& sc,
                                                   f32x16& dpc, const _Float16* Qp, const _Float16* Gp,
                                                   const _Float16* Qc, const _Float16* Gc, const _Float16* Kr,
-                                                  const _Float16* Vr, uint32_t rowx, uint32_t trx0, uint32_t trx1) {
+                                                  const _Float16* Vr, const float* Lc, int lg, uint32_t rowx,
+                                                  uint32_t trx0, uint32_t trx1) {
   constexpr int DM = D / 32, KS = D / 16, L = kLookahead;
   constexpr int NG = 4 * DM;               // gradient products (one operand read each)
   constexpr int NS = 2 * KS;               // score products (two operand reads each)
@@ -369,13 +378,30 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
   f16x8 ring[L];
 #pragma unroll
   for (int j = 0; j < L; ++j) ring[j] = load(j);
-  sc = (f32x16){};
-  dpc = (f32x16){};
+  // S and dP start at their rows' start values (register i: row
+  // 8 (i / 4) + 4 lg + i % 4 of the block), -LSE log2 e / c2 and -D, so the
+  // vector phase takes P = exp2(c2 S) and dS = P dP.  They are read a few
+  // gradient products before the score products (early enough to complete
+  // behind them, late enough not to be held through all of them).
+  constexpr int kStartAt = NG > 8 ? NG - 8 : 0;
+  auto load_start = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 a = *(const f32x4*)(Lc + 8 * i + 4 * lg);
+      const f32x4 b = *(const f32x4*)(Lc + 32 + 8 * i + 4 * lg);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sc[4 * i + j] = a[j];
+        dpc[4 * i + j] = b[j];
+      }
+    }
+  };
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
   int next = L;   // next operand to read
 #pragma unroll
   for (int k = 0; k < NG + NS; ++k) {
+    if (k == kStartAt) load_start();
     int used;   // operands consumed through this product
     if (k < NG) {
       const int c = (k / 2) / DM, dm = (k / 2) % DM;
@@ -538,15 +564,19 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
   char* gstage = smem_raw + C::kResBytes + g * 2 * C::kStageBytes;
   auto Qb = [&](int b) { return (_Float16*)(gstage + b * C::kStageBytes); };
   auto Gb = [&](int b) { return Qb(b) + C::kBlkTile; };
-  auto Lb = [&](int b) { return (float*)(Gb(b) + C::kBlkTile); };   // (LSE log2 e, D scaled) per row
+  auto Lb = [&](int b) { return (float*)(Gb(b) + C::kBlkTile); };   // 32 S, then 32 dP start values
   // The group's step r into buffer b: Q and dO rows and the row terms (rows
   // past N read as zeros: their Q and dO rows are zero, so they add nothing).
   auto stage = [&](int r, int b) {
     const int q0 = blk_at(2 * r + g) * C::BLK;
     dma_rows<D, C::BLK, 4>(h.q, Qb(b), q0, kb, lane);
     dma_rows<D, C::BLK, 4>(h.g, Gb(b), q0, kb, lane);
-    if (kb == 0 && lane < C::BLK * 8 / 16)
-      lds_copy16(h.rt, (uint32_t)(q0 * 8 + 16 * lane), (uint32_t)(uintptr_t)Lb(b));
+    // The block's 32 S start values (lanes 0-7) and 32 dP start values
+    // (lanes 8-15, landing 128 bytes further on).
+    if (kb == 0 && lane < C::BLK / 4)
+      lds_copy16(h.rt0, (uint32_t)(q0 * 4 + 16 * lane), (uint32_t)(uintptr_t)Lb(b));
+    if (kb == 0 && lane >= C::BLK / 4 && lane < C::BLK / 2)
+      lds_copy16(h.rt1, (uint32_t)(q0 * 4 + 16 * (lane - C::BLK / 4)), (uint32_t)(uintptr_t)Lb(b));
   };
 
   // This wave's K / V rows (B operands; row 32 kb + lc has the same chunk
@@ -605,12 +635,13 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
     {
       const int cb = r & 1, pbuf = cb ^ 1;
       dkdv_matrix_phase<D>(dk_acc, dv_acc, pw, dsw, sc, dpc, Qb(pbuf), Gb(pbuf), Qb(cb), Gb(cb), Ks + krow_base,
-                           Vs + krow_base, rowx, trx0, trx1);
+                           Vs + krow_base, Lb(cb), lg, rowx, trx0, trx1);
     }
     __syncthreads();
     // Vector phase: the copy of step r + 1 into the buffer step r - 1 used
-    // (its last reader was the matrix phase just ended); P = exp2(s c2 -
-    // LSE log2 e) and dS = P (dP - D) of step r as fp16 pairs.
+    // (its last reader was the matrix phase just ended); P = exp2(c2 S) and
+    // dS = P dP of step r (S and dP started at their rows' start values) as
+    // fp16 pairs.
     if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
     {
       // A group without a step r masks all its scores (P = dS = 0, so the
@@ -624,23 +655,15 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 8 * (i >> 2) + (i & 3) >= tl ? sc[i] : -INFINITY;
       }
-      const float* Ls = Lb(r & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // Rows 8 i + 4 lg .. + 3: (LSE log2 e, D) pairs.
-        const f32x4 a4 = *(const f32x4*)(Ls + 2 * (8 * i + 4 * lg));
-        const f32x4 b4 = *(const f32x4*)(Ls + 2 * (8 * i + 4 * lg) + 4);
-        const float l4[4] = {a4[0], a4[2], b4[0], b4[2]}, d4[4] = {a4[1], a4[3], b4[1], b4[3]};
-        float p[4], ds[4];
+        float p[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = fast_exp2(__builtin_fmaf(sc[4 * i + j], c2, -l4[j]));
-          ds[j] = p[j] * (dpc[4 * i + j] - d4[j]);
-        }
+        for (int j = 0; j < 4; ++j) p[j] = fast_exp2(sc[4 * i + j] * c2);
         pw[2 * i] = pack_f16x2(p[0], p[1]);
         pw[2 * i + 1] = pack_f16x2(p[2], p[3]);
-        dsw[2 * i] = pack_f16x2(ds[0], ds[1]);
-        dsw[2 * i + 1] = pack_f16x2(ds[2], ds[3]);
+        dsw[2 * i] = pack_f16x2(p[0] * dpc[4 * i], p[1] * dpc[4 * i + 1]);
+        dsw[2 * i + 1] = pack_f16x2(p[2] * dpc[4 * i + 2], p[3] * dpc[4 * i + 3]);
       }
     }
     wait_vmem_all();
@@ -777,13 +800,14 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
   // its LDS slot, 1 KB of consecutive rows per copy (zeros past N); read
   // back below as the B operands.
   dma_rows<D, C::BLK, 1>(g == 0 ? h.q : h.g, (_Float16*)(smem_raw + layout::bwd_dq_qslot<D>(wave)), qw0, 0, lane);
-  // Start values of this lane's S^T and dP^T accumulators: -LSE log2 e / c2
-  // (-inf past N, so P = 0 there) and -D in the scaled dP's units; then
-  // P^T = exp2(c2 S^T) and dS^T = P^T dP^T.
+  // Start values of this lane's S^T and dP^T accumulators (the row terms
+  // the preprocessing wrote): -LSE log2 e / c2 (-inf past N, so P = 0 there)
+  // and -D in the scaled dP's units; then P^T = exp2(c2 S^T) and
+  // dS^T = P^T dP^T.
   float st0 = -INFINITY, dpt0 = 0.f;
   if (q < N) {
-    st0 = -bload32f(h.rt, (uint32_t)q * 8u) / c2;
-    dpt0 = -bload32f(h.rt, (uint32_t)q * 8u + 4u);
+    st0 = bload32f(h.rt0, (uint32_t)q * 4u);
+    dpt0 = bload32f(h.rt1, (uint32_t)q * 4u);
   }
 
   f32x16 dq_acc[DM];
@@ -966,7 +990,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(fa_bwd_convert_kernel<D>, dim3((unsigned)(BH * nch)), dim3(256), 0, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.dout, a.lse, (const float*)a.delta,
-                       (const float*)a.part, a.scales, a.rowterm, (_Float16*)a.q16, (_Float16*)a.do16, a.N, nch);
+                       (const float*)a.part, a.scales, a.rowterm, (_Float16*)a.q16, (_Float16*)a.do16, a.N, nch,
+                       a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.phases & FA_BWD_MAIN) {

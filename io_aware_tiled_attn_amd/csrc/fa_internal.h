@@ -85,8 +85,10 @@ constexpr int kBwdChunkRows = 256;
 //   delta   fp32 [B, H, N]       D_i = sum_c dO_ic O_ic
 //   part    fp32 [B, H, nch, 4]  largest |Q|, |dO|, |K|, |V| of each 256-row chunk
 //   scales  fp32 [B, H, 4]       per-head power-of-two factors of Q, dO, K, V
-//   rowterm fp32 [B, H, N, 2]    per row: LSE log2 e (+inf for a row that saw
-//                                no key) and D times the dO and V factors
+//   rowterm fp32 [B, H, 2, N]    per head two planes of per-row start values
+//                                of the main kernels' accumulators: S at
+//                                -LSE log2 e / c2 (-inf for a row that saw no
+//                                key), dP at -D times the dO and V factors
 //   q16, do16, k16, v16          fp16 [B, H, N, d] each: the inputs times their factors
 struct BwdWorkspace {
   size_t delta, part, scales, rowterm, q16, do16, k16, v16, total;

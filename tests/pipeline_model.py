@@ -152,8 +152,9 @@ def forward_schedule(num_kt, preload_v, ahead=3, copy_at="vector", bufs=3, waits
 # Backward dK/dV kernel: group g walks its steps r (blocks 2 r + g of the
 # visited list) in its own two buffers, step r in buffer r % 2.  Matrix
 # phase of round r: the gradient products of step r - 1 and the score
-# products of step r.  Vector phase: the copy of step r + 1 into buffer
-# (r + 1) % 2, P and dS of step r (reading its row terms), wait for all.
+# products of step r (with the row terms of step r as the accumulators'
+# start values).  Vector phase: the copy of step r + 1 into buffer
+# (r + 1) % 2, P and dS of step r (from registers), wait for all.
 # Steps a group does not have are still computed on a stale buffer (their
 # results are masked to zero).
 # ---------------------------------------------------------------------------
@@ -180,7 +181,6 @@ def dkdv_schedule(n_blk, bufs=2, copy_in_vector=True):
             g.barrier()
             if copy_in_vector and has(r + 1):
                 g.copy(buf(r + 1), (g_i, r + 1))
-            g.read(buf(r), (g_i, r) if has(r) else None)   # row terms
             g.wait("all")
             g.barrier()
         if g_i == 0:
