@@ -17,7 +17,8 @@ backward kernels' figures, the roofline of the dominant kernel (achieved
 against the published peak, with the HBM bytes per launch measured by the
 hardware counters while the kernel sources are unchanged), the CPU oracle's
 throughput on a sample of the same workload, and beside the dense step the
-block-sparse step, the FP8 forward and KV-cache decoding.
+block-sparse step, the FP8 forward, KV-cache decoding and the bf16 forward
+alone at other d = 128 shapes with N >= 4096 (causal and not).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -76,6 +77,8 @@ def parse_args():
                     help="skip the FP8 forward reported beside the dense step")
     ap.add_argument("--no-blocksparse", action="store_true",
                     help="skip the block-sparse step reported beside the dense one")
+    ap.add_argument("--no-fwd-shapes", action="store_true",
+                    help="skip the forward timings at the other d = 128 shapes with N >= 4096")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB once (device to device) so that "
                          "HBM byte counters can be scaled against a transfer of known size")
@@ -286,6 +289,42 @@ def fp8_step(warmup, steps):
     }
 
 
+# Forward-only timings at d = 128 and N >= 4096 besides the step's own shape:
+# (B, H, N, causal), B * H * N fixed at 2^19 query rows.
+FWD_SHAPES = ((4, 32, 4096, False), (2, 32, 8192, True), (2, 32, 8192, False), (1, 32, 16384, True),
+              (1, 32, 16384, False))
+
+
+def forward_shapes_step(warmup, steps):
+    """The bf16 forward alone on seeded N(0,1) inputs of each shape in
+    FWD_SHAPES (drawn on the device, rounded to bf16), timed with events on
+    the launch stream; FLOPs 4 B H N^2 d, halved when causal."""
+    import torch
+    import io_aware_tiled_attn_amd as fa
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(4096)
+    out = []
+    for B, H, N, causal in FWD_SHAPES:
+        q, k, v = (torch.randn((B, H, N, 128), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        for _ in range(warmup):
+            fa.flash_attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fa.flash_attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        tf = 4.0 * B * H * N * N * 128 * (0.5 if causal else 1.0) / (ms * 1e-3) / 1e12
+        out.append({"B": B, "H": H, "N": N, "d": 128, "causal": causal, "ms": round(ms, 4),
+                    "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del q, k, v, o, lse
+    return out
+
+
 def decode_step(warmup, steps):
     """Decoding against a KV cache (split-KV): one new query per head of a
     B=16, H=32, 8192-entry d=128 cache, the inputs drawn with the workload's
@@ -482,6 +521,9 @@ def main():
     if not args.no_fp8:
         print("[bench] FP8 forward", file=sys.stderr, flush=True)
         result["fp8_forward"] = fp8_step(max(5, args.warmup // 2), args.steps)
+    if not args.no_fwd_shapes:
+        print("[bench] forward at other d = 128 shapes", file=sys.stderr, flush=True)
+        result["fwd_d128_shapes"] = forward_shapes_step(max(3, args.warmup // 4), max(10, args.steps // 2))
     if not args.no_decode:
         print("[bench] decoding step", file=sys.stderr, flush=True)
         result["decode"] = decode_step(max(5, args.warmup // 2), args.steps)
