@@ -493,8 +493,17 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(0), voff, kbuf(1), koff);
   if (group == 1) __syncthreads();
 
+  // Causal, dense, d = 128: visited tiles from n_live on hold only keys
+  // after every query of this wave, so their P is zero.  The wave then runs
+  // the P V products of tile n_live - 1 alone and, on the steps after it,
+  // only the copies, waits and barriers every wave takes part in (skipping
+  // exactly zero terms: the result is the same bit for bit).  At d = 64 the
+  // extra loops cost the registers of the second workgroup per CU.
+  constexpr bool kDeadTail = CAUSAL && !SPARSE && D == 128;
+  const int n_live = kDeadTail ? min(num_kt, (q_wave0 + 31) / BN + 1) : num_kt;
   int b_cur = 0;   // t % 3
-  for (int t = 0; t + 1 < num_kt; ++t) {
+  int t = 0;
+  for (; t + 1 < n_live; ++t) {
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;    // (t + 1) % 3
     const int b_after = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
@@ -516,13 +525,43 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __syncthreads();
     b_cur = b_next;
   }
-  // The last step (outside the loop, so the loop's code stays one stream):
-  // O += P V only, there being no next tile; the same two barriers.
+  if constexpr (!kDeadTail) {
+    // The last step (outside the loop, so the loop's code stays one
+    // stream): O += P V only, there being no next tile; the same two
+    // barriers.
+    if (num_kt > 0) {
+      matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload, false>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_cur), koff, qb);
+      __syncthreads();
+      wait_vmem_all();
+      __syncthreads();
+    }
+  } else {
+  // The copies and waits of step t's vector phase, for the steps with no
+  // softmax.
+  auto copies_only = [&]() {
+    const bool copy_next = t + 3 < num_kt;
+    if (copy_next) copy_tile(tile_at(t + 3), b_cur);
+    if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
+    else wait_vmem_all();
+  };
+  // The last live step (outside the loop, so the loop's code stays one
+  // stream): O += P V only, there being no next tile this wave sees; the
+  // same two barriers.
   if (num_kt > 0) {
     matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload, false>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_cur), koff, qb);
     __syncthreads();
-    wait_vmem_all();
+    copies_only();
     __syncthreads();
+    b_cur = b_cur == 2 ? 0 : b_cur + 1;
+    ++t;
+  }
+  // The steps of tiles this wave does not see.
+  for (; t < num_kt; ++t) {
+    __syncthreads();
+    copies_only();
+    __syncthreads();
+    b_cur = b_cur == 2 ? 0 : b_cur + 1;
+  }
   }
   if (group == 0) __syncthreads();
 
