@@ -196,24 +196,26 @@ __device__ __forceinline__ void softmax_first_fp8(const f32x16 (&s)[BN / 32], i3
   l_run = tile_exp_fp8<BN>(s, pb, m_run == -INFINITY ? 0.f : m_run, scale_log2);
 }
 
-// One matrix phase: O^T += V^T(t) P^T(t) (NC DM products) then
-// S^T(t+1) = K(t+1) Q^T (NB KS products), one MFMA stream with the LDS
-// operands read L products ahead.
-template <int D, int BN, int L>
+// One matrix phase: O^T += V^T(t) P^T(t) (NC DM products) then, with
+// SCORES, S^T(t+1) = K(t+1) Q^T (NB KS products), one MFMA stream with the
+// LDS operands read L products ahead.
+template <int D, int BN, int L, bool SCORES = true>
 __device__ __forceinline__ void matrix_phase_fp8(f32x16 (&oacc)[D / 32], const i32x8 (&pb)[BN / 64],
                                                  const uint8_t* Vs, const int (&voff)[D / 32],
                                                  f32x16 (&s)[BN / 32], const uint8_t* Ks,
                                                  const int (&koff)[D / 64][2], const i32x8 (&qb)[D / 64]) {
   using C = Fp8Cfg<D, BN>;
   constexpr int kPv = C::NC * C::DM;
-  constexpr int kAll = kPv + C::NB * C::KS;
+  constexpr int kAll = kPv + (SCORES ? C::NB * C::KS : 0);
   auto load = [&](int i) -> i32x8 {
     if (i < kPv) return lds_vt_operand<D>(Vs + voff[i % C::DM] + 64 * (i / C::DM) * D);
     const int j = i - kPv, ks = j / C::NB, mb = j % C::NB;
     return lds_k_operand(Ks + 32 * mb * D, koff[ks][0], koff[ks][1]);
   };
+  if constexpr (SCORES) {
 #pragma unroll
-  for (int mb = 0; mb < C::NB; ++mb) s[mb] = (f32x16){};
+    for (int mb = 0; mb < C::NB; ++mb) s[mb] = (f32x16){};
+  }
   __builtin_amdgcn_s_setprio(1);
   i32x8 ring[L];
 #pragma unroll
@@ -325,22 +327,48 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   // barrier interval behind group 0; tile t + 3 is copied into buffer t % 3
   // from the start of step t's vector phase, and at that phase's end each
   // wave waits for all its copies but that one.
+  //
+  // Under the causal mask the tiles from n_live on hold only keys after
+  // every query of this wave (their P is zero): the wave runs the P V
+  // products of tile n_live - 1 alone and, on the steps after it, only its
+  // copies, waits and barriers.  The last step has no next tile's scores to
+  // compute either way.
+  const int n_live = CAUSAL ? min(num_kt, (q_wave0 + 31) / BN + 1) : num_kt;
   if (group == 1) __syncthreads();
   int b_cur = 0;
-  for (int t = 0; t < num_kt; ++t) {
+  int t = 0;
+  for (; t + 1 < n_live; ++t) {
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;
     matrix_phase_fp8<D, BN, 3>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     const bool copy_next = t + 3 < num_kt;
     if (copy_next) copy_tile(t + 3, b_cur);
-    if (t + 1 < num_kt) {
-      if (masked(t + 1)) mask_tile_fp8<BN>(s, (t + 1) * BN, qlim, lg);
-      softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
-    }
+    if (masked(t + 1)) mask_tile_fp8<BN>(s, (t + 1) * BN, qlim, lg);
+    softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
     else wait_vmem_all();
     __syncthreads();
     b_cur = b_next;
+  }
+  auto copies_only = [&]() {
+    const bool copy_next = t + 3 < num_kt;
+    if (copy_next) copy_tile(t + 3, b_cur);
+    if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
+    else wait_vmem_all();
+  };
+  if (num_kt > 0) {
+    matrix_phase_fp8<D, BN, 3, false>(oacc, pb, vbuf(b_cur), voff, s, kbuf(b_cur), koff, qb);
+    __syncthreads();
+    copies_only();
+    __syncthreads();
+    b_cur = b_cur == 2 ? 0 : b_cur + 1;
+    ++t;
+  }
+  for (; t < num_kt; ++t) {
+    __syncthreads();
+    copies_only();
+    __syncthreads();
+    b_cur = b_cur == 2 ? 0 : b_cur + 1;
   }
   if (group == 0) __syncthreads();
 
