@@ -354,8 +354,9 @@ constexpr int kLookahead = 8;
 // dK/dV kernel.  Operands: per (c, dm) of the gradient products dO^T then
 // Q^T (transposing reads of the previous block, rows 16 c .. 16 c + 15),
 // then per k-step Q, K, dO, V rows (Q, dO of the current block; K, V
-// resident, already offset to this wave's key block).
-template <int D>
+// resident, already offset to this wave's key block).  GRADS / SCORES
+// false: the stream without the gradient / the score-side products.
+template <int D, bool GRADS = true, bool SCORES = true>
 __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x16 (&dv_acc)[D / 32],
                                                   const uint32_t (&pw)[8], const uint32_t (&dsw)[8], f32x16& sc,
                                                   f32x16& dpc, const _Float16* Qp, const _Float16* Gp,
@@ -363,8 +364,8 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
                                                   const _Float16* Vr, const float* Lc, int lg, uint32_t rowx,
                                                   uint32_t trx0, uint32_t trx1) {
   constexpr int DM = D / 32, KS = D / 16, L = kLookahead;
-  constexpr int NG = 4 * DM;               // gradient products (one operand read each)
-  constexpr int NS = 2 * KS;               // score products (two operand reads each)
+  constexpr int NG = GRADS ? 4 * DM : 0;   // gradient products (one operand read each)
+  constexpr int NS = SCORES ? 2 * KS : 0;  // score products (two operand reads each)
   constexpr int NL = NG + 2 * NS;          // operand reads
   auto load = [&](int j) -> f16x8 {
     if (j < NG) {
@@ -377,7 +378,7 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
   };
   f16x8 ring[L];
 #pragma unroll
-  for (int j = 0; j < L; ++j) ring[j] = load(j);
+  for (int j = 0; j < L && j < NL; ++j) ring[j] = load(j);
   // S and dP start at their rows' start values (register i: row
   // 8 (i / 4) + 4 lg + i % 4 of the block), -LSE log2 e / c2 and -D, so the
   // vector phase takes P = exp2(c2 S) and dS = P dP.  They are read a few
@@ -401,7 +402,7 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
   int next = L;   // next operand to read
 #pragma unroll
   for (int k = 0; k < NG + NS; ++k) {
-    if (k == kStartAt) load_start();
+    if (SCORES && k == kStartAt) load_start();
     int used;   // operands consumed through this product
     if (k < NG) {
       const int c = (k / 2) / DM, dm = (k / 2) % DM;
@@ -425,17 +426,17 @@ __device__ __forceinline__ void dkdv_matrix_phase(f32x16 (&dk_acc)[D / 32], f32x
 }
 
 // dQ kernel.  Operands: per (c, dm) K^T (transposing read of the previous
-// block), then per k-step K and V rows of the current block; Q and dO are
-// the register B operands.  The score accumulators start at st0 and dpt0
-// (the lane's query's -LSE log2 e / c2 and -D) instead of zero.
-template <int D>
+// block), then (SCORES) per k-step K and V rows of the current block; Q and
+// dO are the register B operands.  The score accumulators start at st0 and
+// dpt0 (the lane's query's -LSE log2 e / c2 and -D) instead of zero.
+template <int D, bool SCORES = true>
 __device__ __forceinline__ void dq_matrix_phase(f32x16 (&dq_acc)[D / 32], const uint32_t (&dsw)[8], f32x16& st,
                                                 f32x16& dpt, const f16x8 (&qbf)[D / 16], const f16x8 (&gbf)[D / 16],
                                                 const _Float16* Kp, const _Float16* Kc, const _Float16* Vc,
                                                 uint32_t rowx, uint32_t trx0, uint32_t trx1, float st0, float dpt0) {
   constexpr int DM = D / 32, KS = D / 16, L = kLookahead;
   constexpr int NG = 2 * DM;
-  constexpr int NS = 2 * KS;
+  constexpr int NS = SCORES ? 2 * KS : 0;
   constexpr int NL = NG + NS;              // one operand read per product
   auto load = [&](int j) -> f16x8 {
     if (j < NG) {
@@ -447,14 +448,16 @@ __device__ __forceinline__ void dq_matrix_phase(f32x16 (&dq_acc)[D / 32], const 
   };
   f16x8 ring[L];
 #pragma unroll
-  for (int j = 0; j < L; ++j) ring[j] = load(j);
+  for (int j = 0; j < L && j < NL; ++j) ring[j] = load(j);
   // (An empty asm per phase keeps the compiler from holding splatted copies
   // of the start values across the loop.)
-  asm volatile("" : "+v"(st0), "+v"(dpt0));
+  if constexpr (SCORES) {
+    asm volatile("" : "+v"(st0), "+v"(dpt0));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    st[i] = st0;
-    dpt[i] = dpt0;
+    for (int i = 0; i < 16; ++i) {
+      st[i] = st0;
+      dpt[i] = dpt0;
+    }
   }
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
@@ -630,7 +633,63 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
   wait_vmem_all();
   __syncthreads();
   if (g == 1) __syncthreads();
-  for (int r = 0; r <= R; ++r) {
+  // P = exp2(c2 S) and dS = P dP of step r (S and dP started at their rows'
+  // start values) as fp16 pairs.
+  auto scores_to_p = [&](int r) {
+    // Keys past N and (causal) keys after the query: P = 0.  The query
+    // offset of register i is 8 (i / 4) + 4 lg + i % 4.
+    const int qw0 = blk_at(2 * r + g) * C::BLK;
+    if ((kw0 + 31 >= N) || (CAUSAL && qw0 < kw0 + 31)) {
+      const int tl = !key_ok ? 64 : (CAUSAL ? key - qw0 - 4 * lg : -64);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = 8 * (i >> 2) + (i & 3) >= tl ? sc[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = fast_exp2(sc[4 * i + j] * c2);
+      pw[2 * i] = pack_f16x2(p[0], p[1]);
+      pw[2 * i + 1] = pack_f16x2(p[2], p[3]);
+      dsw[2 * i] = pack_f16x2(p[0] * dpc[4 * i], p[1] * dpc[4 * i + 1]);
+      dsw[2 * i + 1] = pack_f16x2(p[2] * dpc[4 * i + 2], p[3] * dpc[4 * i + 3]);
+    }
+  };
+  // The copy of step r + 1 into the buffer step r - 1 used (its last reader
+  // was the matrix phase just ended).
+  auto stage_next = [&](int r) {
+    if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
+  };
+  // The group's steps are r < n_valid; round r runs the gradient products
+  // of step r - 1 and the score-side products of step r, so the first round
+  // has no gradient products and round n_valid no score products.  Under
+  // the causal mask (dense) the first d0 steps of this wave are query
+  // blocks that end before its first key (P = dS = 0): it runs only its
+  // share of the copies, the waits and the barriers on those rounds, and
+  // its first live round has no gradient products either (skipping exact
+  // zeros: the result is the same bit for bit).  Rounds past n_valid only
+  // keep the barriers.
+  const int n_valid = (n_blk - g + 1) / 2;
+  int d0 = 0;
+  if constexpr (CAUSAL && !SPARSE) d0 = min(n_valid, kb > g ? (kb - g + 1) / 2 : 0);
+  int r = 0;
+  for (; r < d0; ++r) {
+    __syncthreads();
+    stage_next(r);
+    wait_vmem_all();
+    __syncthreads();
+  }
+  if (r < n_valid) {
+    dkdv_matrix_phase<D, false, true>(dk_acc, dv_acc, pw, dsw, sc, dpc, Qb(0), Gb(0), Qb(r & 1), Gb(r & 1),
+                                      Ks + krow_base, Vs + krow_base, Lb(r & 1), lg, rowx, trx0, trx1);
+    __syncthreads();
+    stage_next(r);
+    scores_to_p(r);
+    wait_vmem_all();
+    __syncthreads();
+    ++r;
+  }
+  for (; r < n_valid; ++r) {
     // Matrix phase: dV and dK of step r - 1; S and dP of step r.
     {
       const int cb = r & 1, pbuf = cb ^ 1;
@@ -638,35 +697,26 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
                            Vs + krow_base, Lb(cb), lg, rowx, trx0, trx1);
     }
     __syncthreads();
-    // Vector phase: the copy of step r + 1 into the buffer step r - 1 used
-    // (its last reader was the matrix phase just ended); P = exp2(c2 S) and
-    // dS = P dP of step r (S and dP started at their rows' start values) as
-    // fp16 pairs.
-    if (valid(r + 1)) stage(r + 1, (r + 1) & 1);
-    {
-      // A group without a step r masks all its scores (P = dS = 0, so the
-      // next gradient products add nothing).  Otherwise keys past N and
-      // (causal) keys after the query: P = 0.  The query offset of register
-      // i is 8 (i / 4) + 4 lg + i % 4.
-      const bool has = valid(r);
-      const int qw0 = has ? blk_at(2 * r + g) * C::BLK : 0;
-      if (!has || (kw0 + 31 >= N) || (CAUSAL && qw0 < kw0 + 31)) {
-        const int tl = (!has || !key_ok) ? 64 : (CAUSAL ? key - qw0 - 4 * lg : -64);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = 8 * (i >> 2) + (i & 3) >= tl ? sc[i] : -INFINITY;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = fast_exp2(sc[4 * i + j] * c2);
-        pw[2 * i] = pack_f16x2(p[0], p[1]);
-        pw[2 * i + 1] = pack_f16x2(p[2], p[3]);
-        dsw[2 * i] = pack_f16x2(p[0] * dpc[4 * i], p[1] * dpc[4 * i + 1]);
-        dsw[2 * i + 1] = pack_f16x2(p[2] * dpc[4 * i + 2], p[3] * dpc[4 * i + 3]);
-      }
-    }
+    // Vector phase: the next copy, P and dS of step r, the wait.
+    stage_next(r);
+    scores_to_p(r);
     wait_vmem_all();
+    __syncthreads();
+  }
+  // Round n_valid: the gradient products of the last step.
+  if (r <= R) {
+    if (n_valid > d0) {
+      const int pbuf = (r & 1) ^ 1;
+      dkdv_matrix_phase<D, true, false>(dk_acc, dv_acc, pw, dsw, sc, dpc, Qb(pbuf), Gb(pbuf), Qb(0), Gb(0),
+                                        Ks + krow_base, Vs + krow_base, Lb(0), lg, rowx, trx0, trx1);
+    }
+    __syncthreads();
+    wait_vmem_all();
+    __syncthreads();
+    ++r;
+  }
+  for (; r <= R; ++r) {
+    __syncthreads();
     __syncthreads();
   }
   if (g == 0) __syncthreads();
@@ -876,38 +926,78 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
   }
   if (g == 1) __syncthreads();
   int cb = 0;   // r % 3
-  for (int r = 0; r <= R; ++r) {
+  // P^T and dS^T of step r (the vector phase's arithmetic).
+  auto scores_to_ds = [&](int r) {
+    // A group without a step r masks all its scores (P = dS = 0).
+    // Otherwise keys past N and (causal) keys after the query: P = 0.
+    // The key offset of register i is 8 (i / 4) + 4 lg + i % 4.
+    const bool has = valid(r);
+    const int kw0 = has ? blk_at(2 * r + g) * C::BLK : 0;
+    if (!has || (kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qw0)) {
+      const int tl = has ? min(N - 1, CAUSAL ? q : N - 1) - kw0 - 4 * lg : -64;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st_acc[i] = 8 * (i >> 2) + (i & 3) <= tl ? st_acc[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(st_acc[2 * i] * c2);
+      const float p1 = fast_exp2(st_acc[2 * i + 1] * c2);
+      dsw[i] = pack_f16x2(p0 * dpt[2 * i], p1 * dpt[2 * i + 1]);
+    }
+  };
+  // The copy of step r + 2 into the buffer step r - 1 used (its last reader
+  // was the matrix phase just ended), then the wait: step r + 1's copy
+  // (issued a step ago) has landed; step r + 2's may still be in flight
+  // (the loop issues no other memory loads).
+  auto copy_and_wait = [&](int r, int pbuf) {
+    const bool copy = valid(r + 2);
+    if (copy) stage(r + 2, pbuf);
+    return copy;
+  };
+  auto wait_copies = [&](bool copy) {
+    if (copy) wait_vmem_keep<kCopies>();
+    else wait_vmem_all();
+  };
+  // Round r runs the dQ products of step r - 1 and the score-side products
+  // of step r.  The wave's steps are r < n_live: the group's steps (blocks
+  // 2 r + g up to the last visited one) and, under the causal mask (dense),
+  // only those up to its last query's key block; the later blocks hold no
+  // key it sees (P = dS = 0).  Round n_live runs the dQ products of step
+  // n_live - 1 alone, the rounds after it only the copies, waits and
+  // barriers every wave takes part in (skipping exact zeros: the result is
+  // the same bit for bit).
+  int lb = n_blk - 1;   // last visited block with a key the wave sees
+  if constexpr (CAUSAL && !SPARSE) lb = min(lb, (qw0 + 31) / C::BLK);
+  const int n_live = lb >= g ? (lb - g) / 2 + 1 : 0;
+  int r = 0;
+  for (; r < n_live; ++r) {
     const int pbuf = cb == 0 ? 2 : cb - 1, nbuf = cb == 2 ? 0 : cb + 1;   // (r - 1) % 3, (r + 1) % 3
     // Matrix phase: dQ^T of step r - 1; S^T and dP^T of step r.
     dq_matrix_phase<D>(dq_acc, dsw, st_acc, dpt, qbf, gbf, Kb(pbuf), Kb(cb), Vb(cb), rowx, trx0, trx1, st0, dpt0);
     __syncthreads();
-    // Vector phase: the copy of step r + 2 into the buffer step r - 1 used
-    // (its last reader was the matrix phase just ended); P^T = exp2(c2 S^T)
-    // and dS^T = P^T dP^T of step r as fp16 pairs.
-    const bool copy = valid(r + 2);
-    if (copy) stage(r + 2, pbuf);
-    {
-      // A group without a step r masks all its scores (P = dS = 0).
-      // Otherwise keys past N and (causal) keys after the query: P = 0.
-      // The key offset of register i is 8 (i / 4) + 4 lg + i % 4.
-      const bool has = valid(r);
-      const int kw0 = has ? blk_at(2 * r + g) * C::BLK : 0;
-      if (!has || (kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qw0)) {
-        const int tl = has ? min(N - 1, CAUSAL ? q : N - 1) - kw0 - 4 * lg : -64;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st_acc[i] = 8 * (i >> 2) + (i & 3) <= tl ? st_acc[i] : -INFINITY;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(st_acc[2 * i] * c2);
-        const float p1 = fast_exp2(st_acc[2 * i + 1] * c2);
-        dsw[i] = pack_f16x2(p0 * dpt[2 * i], p1 * dpt[2 * i + 1]);
-      }
-    }
-    // Step r + 1's copy (issued a step ago) has landed; step r + 2's may
-    // still be in flight (this loop issues no other memory loads).
-    if (copy) wait_vmem_keep<kCopies>();
-    else wait_vmem_all();
+    // Vector phase: the next copy, P^T = exp2(c2 S^T) and dS^T = P^T dP^T
+    // of step r as fp16 pairs, the wait.
+    const bool copy = copy_and_wait(r, pbuf);
+    scores_to_ds(r);
+    wait_copies(copy);
+    __syncthreads();
+    cb = nbuf;
+  }
+  if (r <= R) {
+    const int pbuf = cb == 0 ? 2 : cb - 1, nbuf = cb == 2 ? 0 : cb + 1;
+    if (n_live > 0)
+      dq_matrix_phase<D, false>(dq_acc, dsw, st_acc, dpt, qbf, gbf, Kb(pbuf), Kb(cb), Vb(cb), rowx, trx0, trx1,
+                                st0, dpt0);
+    __syncthreads();
+    wait_copies(copy_and_wait(r, pbuf));
+    __syncthreads();
+    cb = nbuf;
+    ++r;
+  }
+  for (; r <= R; ++r) {
+    const int pbuf = cb == 0 ? 2 : cb - 1, nbuf = cb == 2 ? 0 : cb + 1;
+    __syncthreads();
+    wait_copies(copy_and_wait(r, pbuf));
     __syncthreads();
     cb = nbuf;
   }

@@ -158,8 +158,11 @@ def forward_schedule(num_kt, preload_v, ahead=3, copy_at="vector", bufs=3, waits
 # products of step r (with the row terms of step r as the accumulators'
 # start values).  Vector phase: the copy of step r + 1 into buffer
 # (r + 1) % 2, P and dS of step r (from registers), wait for all.
-# Steps a group does not have are still computed on a stale buffer (their
-# results are masked to zero).
+# A wave runs no products for steps its group does not have, nor for the
+# causal steps whose queries all come before its keys, nor the gradient
+# products of round 0 or the score products past its last step; it still
+# issues its share of every copy and passes every wait and barrier, so the
+# model (which keeps every read) covers it.
 # ---------------------------------------------------------------------------
 def dkdv_schedule(n_blk, bufs=2, copy_in_vector=True):
     R = (n_blk + 1) // 2
@@ -193,7 +196,8 @@ def dkdv_schedule(n_blk, bufs=2, copy_in_vector=True):
 
 # ---------------------------------------------------------------------------
 # Backward dQ kernel: three buffers per group, step r in buffer r % 3,
-# steps 0 and 1 copied before the loop.  Vector phase of round r: the copy
+# steps 0 and 1 copied before the loop (as above, a wave skips the products
+# of steps it has no key of, never a copy, wait or barrier).  Vector phase of round r: the copy
 # of step r + 2 into buffer (r + 2) % 3 (that of step r - 1), then a wait
 # that leaves only that copy in flight (or drains all when none was issued).
 # ---------------------------------------------------------------------------
