@@ -79,6 +79,15 @@ __device__ __forceinline__ float abs_max_bf16x2(float m, uint32_t w) {
   return fmaxf(m, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
 }
 
+// bf16 pair times f, rounded to an fp16 pair.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float f) {
+  return pack_f16x2(bf16_lo(w) * f, bf16_hi(w) * f);
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float f) {
+  return (u32x4){bf16x2_to_f16x2(x[0], f), bf16x2_to_f16x2(x[1], f), bf16x2_to_f16x2(x[2], f),
+                 bf16x2_to_f16x2(x[3], f)};
+}
+
 // Largest value of x over the workgroup (NW waves), returned to every
 // thread.  red: NW floats of LDS.
 template <int NW>
@@ -95,54 +104,81 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Per 256-row chunk of a head: D_i = sum_c dO_ic O_ic and the largest
-//    |Q|, |dO|, |K|, |V| of the chunk.
+// 1. Per 256-row chunk of a head: D_i = sum_c dO_ic O_ic, the largest |Q|,
+//    |dO|, |K|, |V| of the chunk, and the chunk's rows of Q and dO as fp16
+//    times the chunk's own factors (held in registers from the one read of
+//    them; kernel 2 redoes the chunks whose factor is not the head's).
 // ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 512;
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kPrepThreads)
 fa_bwd_prep_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const __bf16* __restrict__ Q,
                    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ delta,
-                   float* __restrict__ part, int N, int nch) {
-  constexpr int TPR = D / 8;          // threads per row, 8 elements each
-  constexpr int RPI = 256 / TPR;      // rows per pass
-  __shared__ float red[4];
+                   float* __restrict__ part, _Float16* __restrict__ Q16, _Float16* __restrict__ dO16, int N,
+                   int nch) {
+  constexpr int TPR = D / 8;                   // threads per row, 8 elements each
+  constexpr int RPI = kPrepThreads / TPR;      // rows per pass
+  constexpr int NP = kBwdChunkRows / RPI;      // passes per chunk
+  constexpr int NW = kPrepThreads / 64;
+  __shared__ float red[NW];
   const int bh = blockIdx.x / nch, ch = blockIdx.x % nch;
   const int tid = threadIdx.x, col = (tid % TPR) * 8;
   const int row0 = ch * kBwdChunkRows;
   const int rows = min(kBwdChunkRows, N - row0);
   float m[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int r = tid / TPR; r < rows; r += RPI) {
-    const size_t off = ((size_t)bh * N + row0 + r) * D + col;
-    const u32x4 o = *(const u32x4*)(O + off);
-    const u32x4 g = *(const u32x4*)(dO + off);
-    const u32x4 qv = *(const u32x4*)(Q + off);
-    const u32x4 kv = *(const u32x4*)(K + off);
-    const u32x4 vv = *(const u32x4*)(V + off);
-    float acc = 0.f;
+  u32x4 qk[NP], gk[NP];   // this thread's Q and dO chunks of the chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
-      m[0] = abs_max_bf16x2(m[0], qv[i]);
-      m[1] = abs_max_bf16x2(m[1], g[i]);
-      m[2] = abs_max_bf16x2(m[2], kv[i]);
-      m[3] = abs_max_bf16x2(m[3], vv[i]);
+  for (int p = 0; p < NP; ++p) {
+    const int r = tid / TPR + p * RPI;
+    qk[p] = gk[p] = (u32x4){0u, 0u, 0u, 0u};
+    if (r < rows) {
+      const size_t off = ((size_t)bh * N + row0 + r) * D + col;
+      const u32x4 o = *(const u32x4*)(O + off);
+      const u32x4 g = *(const u32x4*)(dO + off);
+      const u32x4 qv = *(const u32x4*)(Q + off);
+      const u32x4 kv = *(const u32x4*)(K + off);
+      const u32x4 vv = *(const u32x4*)(V + off);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
+        m[0] = abs_max_bf16x2(m[0], qv[i]);
+        m[1] = abs_max_bf16x2(m[1], g[i]);
+        m[2] = abs_max_bf16x2(m[2], kv[i]);
+        m[3] = abs_max_bf16x2(m[3], vv[i]);
+      }
+      qk[p] = qv;
+      gk[p] = g;
+      // The TPR threads of a row share r, so they run this together.
+#pragma unroll
+      for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2);
+      if (tid % TPR == 0) delta[(size_t)bh * N + row0 + r] = acc;
     }
-    // The TPR threads of a row share r, so they run this together.
-#pragma unroll
-    for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2);
-    if (tid % TPR == 0) delta[(size_t)bh * N + row0 + r] = acc;
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    m[t] = block_max<4>(m[t], red);
+    m[t] = block_max<NW>(m[t], red);
     if (tid == 0) part[((size_t)bh * nch + ch) * 4 + t] = m[t];
+  }
+  const float fq = pow2_scale_for(m[0]), fg = pow2_scale_for(m[1]);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int r = tid / TPR + p * RPI;
+    if (r < rows) {
+      const size_t off = ((size_t)bh * N + row0 + r) * D + col;
+      *(u32x4*)(Q16 + off) = bf16x8_to_f16x8(qk[p], fq);
+      *(u32x4*)(dO16 + off) = bf16x8_to_f16x8(gk[p], fg);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. Per 256-row chunk of a head: the head's factors (from all its chunk
-//    maxima), the chunk's rows of Q and dO times their factors as fp16,
-//    and its row terms, in two planes of N floats per head: the start value
+//    maxima); where the chunk's own factor for Q or dO (the one kernel 1
+//    converted it with) is not the head's, the chunk's rows of that tensor
+//    again from the bf16 source, times the head's factor (so every fp16 copy
+//    is the bf16 value times the head's factor, rounded once); and its row
+//    terms, in two planes of N floats per head: the start value
 //    of the row's S accumulator, -LSE log2 e / c2 with c2 the exponent's
 //    multiplier of the scaled S (-inf for a row that saw no key, so that
 //    P = exp2(c2 S) = 0 there), and of its dP accumulator, -D times the dO
@@ -182,15 +218,13 @@ fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ d
   const __bf16* src[2] = {Q, dO};
   _Float16* dst[2] = {Q16, dO16};
   const int n8 = rows * (D / 8);
-  for (int i = tid; i < n8; i += 256) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x4 x = *(const u32x4*)(src[t] + rbase * D + 8 * (size_t)i);
-      u32x4 y;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) y[w] = pack_f16x2(bf16_lo(x[w]) * f[t], bf16_hi(x[w]) * f[t]);
-      *(u32x4*)(dst[t] + rbase * D + 8 * (size_t)i) = y;
-    }
+  for (int t = 0; t < 2; ++t) {
+    // The same float kernel 1 computed, so the same factor.
+    const float own = pow2_scale_for(part[((size_t)bh * nch + ch) * 4 + t]);
+    if (own == f[t]) continue;
+    for (int i = tid; i < n8; i += 256)
+      *(u32x4*)(dst[t] + rbase * D + 8 * (size_t)i) = bf16x8_to_f16x8(*(const u32x4*)(src[t] + rbase * D + 8 * (size_t)i), f[t]);
   }
 }
 
@@ -291,15 +325,6 @@ __device__ __forceinline__ BwdHead bwd_head(const _Float16* Q16, const _Float16*
   h.rt0 = make_rsrc(rowterm + (size_t)2 * bh * N, (uint32_t)N * 4u);
   h.rt1 = make_rsrc(rowterm + (size_t)2 * bh * N + N, (uint32_t)N * 4u);
   return h;
-}
-
-// bf16 pair times f, rounded to an fp16 pair.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float f) {
-  return pack_f16x2(bf16_lo(w) * f, bf16_hi(w) * f);
-}
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float f) {
-  return (u32x4){bf16x2_to_f16x2(x[0], f), bf16x2_to_f16x2(x[1], f), bf16x2_to_f16x2(x[2], f),
-                 bf16x2_to_f16x2(x[3], f)};
 }
 
 // Rows row0 .. row0 + ROWS of an fp16 [., D] head into a permuted LDS tile,
@@ -1074,9 +1099,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   const _Float16* v16 = (const _Float16*)a.v16;
   const _Float16* do16 = (const _Float16*)a.do16;
   if (a.phases & FA_BWD_PREPROCESS) {
-    hipLaunchKernelGGL(fa_bwd_prep_kernel<D>, dim3((unsigned)(BH * nch)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL(fa_bwd_prep_kernel<D>, dim3((unsigned)(BH * nch)), dim3(kPrepThreads), 0, a.stream,
                        (const __bf16*)a.o, (const __bf16*)a.dout, (const __bf16*)a.q, (const __bf16*)a.k,
-                       (const __bf16*)a.v, a.delta, a.part, a.N, nch);
+                       (const __bf16*)a.v, a.delta, a.part, (_Float16*)a.q16, (_Float16*)a.do16, a.N, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(fa_bwd_convert_kernel<D>, dim3((unsigned)(BH * nch)), dim3(256), 0, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.dout, a.lse, (const float*)a.delta,
