@@ -100,6 +100,28 @@ def test_backward_sharp_scale(causal):
     check_grads(inp, causal, grads, [(0, 0), (0, 1)], scale=0.2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_chunks_of_different_magnitude(d):
+    """The preprocessing converts each 256-row chunk of Q and dO to fp16
+    with the chunk's own power-of-two factor and then converts again, with
+    the head's factor, every chunk whose factor differs.  Rows 256-511 of Q
+    scaled by 2^-6 and rows 512-767 of dO by 2^-5 (exact in bf16) give
+    those chunks factors 64 and 32 times the head's: a chunk left at its own
+    factor would scale its scores or its dO by that much."""
+    shape = (1, 2, 1100, d)
+    inp = wl.make_inputs(shape, 4500 + d, "bf16", with_grad=True)
+    q = f64(inp["q"], "bf16")
+    g = f64(inp["do"], "bf16")
+    q[:, :, 256:512] *= 2.0 ** -6
+    g[:, :, 512:768] *= 2.0 ** -5
+    inp = dict(inp, q=wl.f32_to_bf16_bits(q.astype(np.float32)), do=wl.f32_to_bf16_bits(g.astype(np.float32)))
+    assert np.array_equal(f64(inp["q"], "bf16"), q) and np.array_equal(f64(inp["do"], "bf16"), g)
+    announce(f"bwd shape={shape} chunk magnitudes")
+    for causal in (True, False):
+        grads = run_fwd_bwd(inp, causal)
+        check_grads(inp, causal, grads, [(0, 0), (0, 1)])
+
+
 def _invariants(inp, grads, causal):
     """Properties at any size: rows of dS sum to 0 so the key gradients sum
     to 0; rows of P sum to 1 so sum_j dV_j = sum_i dO_i; causal row 0 sees
