@@ -88,19 +88,22 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float f) {
                  bf16x2_to_f16x2(x[3], f)};
 }
 
-// Largest value of x over the workgroup (NW waves), returned to every
-// thread.  red: NW floats of LDS.
+// Largest value of each of m[0..3] over the workgroup (NW waves), in place
+// for every thread.  red: NW float4s of LDS.
 template <int NW>
-__device__ __forceinline__ float block_max(float x, float* red) {
+__device__ __forceinline__ void block_max4(float (&m)[4], f32x4* red) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  __syncthreads();   // red may still be read by a previous call
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m[t] = fmaxf(m[t], __shfl_xor(m[t], off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = (f32x4){m[0], m[1], m[2], m[3]};
   __syncthreads();
-  float m = red[0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
-  return m;
+  for (int i = 0; i < NW; ++i) {
+    const f32x4 r = red[i];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m[t] = fmaxf(m[t], r[t]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -120,7 +123,7 @@ fa_bwd_prep_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, 
   constexpr int RPI = kPrepThreads / TPR;      // rows per pass
   constexpr int NP = kBwdChunkRows / RPI;      // passes per chunk
   constexpr int NW = kPrepThreads / 64;
-  __shared__ float red[NW];
+  __shared__ f32x4 red[NW];
   const int bh = blockIdx.x / nch, ch = blockIdx.x % nch;
   const int tid = threadIdx.x, col = (tid % TPR) * 8;
   const int row0 = ch * kBwdChunkRows;
@@ -155,11 +158,8 @@ fa_bwd_prep_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, 
       if (tid % TPR == 0) delta[(size_t)bh * N + row0 + r] = acc;
     }
   }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    m[t] = block_max<NW>(m[t], red);
-    if (tid == 0) part[((size_t)bh * nch + ch) * 4 + t] = m[t];
-  }
+  block_max4<NW>(m, red);
+  if (tid < 4) part[((size_t)bh * nch + ch) * 4 + tid] = m[tid];
   const float fq = pow2_scale_for(m[0]), fg = pow2_scale_for(m[1]);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -191,15 +191,18 @@ fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ d
                       const float* __restrict__ delta, const float* __restrict__ part, float* __restrict__ scales,
                       float* __restrict__ rowterm, _Float16* __restrict__ Q16, _Float16* __restrict__ dO16, int N,
                       int nch, float scale_log2) {
-  __shared__ float red[4];
   const int bh = blockIdx.x / nch, ch = blockIdx.x % nch;
   const int tid = threadIdx.x;
+  // Every wave takes the head's maxima over its chunks by itself (a few
+  // dozen floats), with no barrier.
   float f[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     float m = 0.f;
-    for (int i = tid; i < nch; i += 256) m = fmaxf(m, part[((size_t)bh * nch + i) * 4 + t]);
-    f[t] = pow2_scale_for(block_max<4>(m, red));
+    for (int i = tid & 63; i < nch; i += 64) m = fmaxf(m, part[((size_t)bh * nch + i) * 4 + t]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    f[t] = pow2_scale_for(m);
   }
   if (ch == 0 && tid == 0) {
 #pragma unroll
