@@ -128,35 +128,46 @@ fa_bwd_prep_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, 
   const int tid = threadIdx.x, col = (tid % TPR) * 8;
   const int row0 = ch * kBwdChunkRows;
   const int rows = min(kBwdChunkRows, N - row0);
+  // Buffer loads over the head: rows past N read as zero, so the passes
+  // need no bounds test and all of their loads can be in flight at once.
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_off, head_bytes), rg = make_rsrc(dO + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off, head_bytes), rk = make_rsrc(K + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_off, head_bytes);
   float m[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[NP];
   u32x4 qk[NP], gk[NP];   // this thread's Q and dO chunks of the chunk
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int r = tid / TPR + p * RPI;
-    qk[p] = gk[p] = (u32x4){0u, 0u, 0u, 0u};
-    if (r < rows) {
-      const size_t off = ((size_t)bh * N + row0 + r) * D + col;
-      const u32x4 o = *(const u32x4*)(O + off);
-      const u32x4 g = *(const u32x4*)(dO + off);
-      const u32x4 qv = *(const u32x4*)(Q + off);
-      const u32x4 kv = *(const u32x4*)(K + off);
-      const u32x4 vv = *(const u32x4*)(V + off);
-      float acc = 0.f;
+    // (Rows past the chunk take the first offset past the head, so no
+    // offset wraps around 2^32.)
+    const uint32_t off = r < rows ? (uint32_t)((row0 + r) * D + col) * 2u : head_bytes;
+    const u32x4 o = bload128(ro, off), g = bload128(rg, off), qv = bload128(rq, off);
+    const u32x4 kv = bload128(rk, off), vv = bload128(rv, off);
+    acc[p] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
-        m[0] = abs_max_bf16x2(m[0], qv[i]);
-        m[1] = abs_max_bf16x2(m[1], g[i]);
-        m[2] = abs_max_bf16x2(m[2], kv[i]);
-        m[3] = abs_max_bf16x2(m[3], vv[i]);
-      }
-      qk[p] = qv;
-      gk[p] = g;
-      // The TPR threads of a row share r, so they run this together.
-#pragma unroll
-      for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2);
-      if (tid % TPR == 0) delta[(size_t)bh * N + row0 + r] = acc;
+    for (int i = 0; i < 4; ++i) {
+      acc[p] += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
+      m[0] = abs_max_bf16x2(m[0], qv[i]);
+      m[1] = abs_max_bf16x2(m[1], g[i]);
+      m[2] = abs_max_bf16x2(m[2], kv[i]);
+      m[3] = abs_max_bf16x2(m[3], vv[i]);
     }
+    qk[p] = qv;
+    gk[p] = g;
+  }
+  // D of each row: the TPR threads of a row hold its partial sums.
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+#pragma unroll
+    for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) acc[p] += __shfl_xor(acc[p], o2);
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int r = tid / TPR + p * RPI;
+    if (tid % TPR == 0 && r < rows) delta[(size_t)bh * N + row0 + r] = acc[p];
   }
   block_max4<NW>(m, red);
   if (tid < 4) part[((size_t)bh * nch + ch) * 4 + tid] = m[tid];
