@@ -638,13 +638,13 @@ fa_bwd_dkdv_kernel(const _Float16* __restrict__ Q16, const __bf16* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) pw[i] = dsw[i] = 0u;
 
-  // The group's first block into buffer 0; zeros into the buffers a round
-  // reads before any block was copied there (buffer 1 in round 0's gradient
-  // products, buffer 0 when the group has no block): finite operands for
-  // the products a group runs without a block.  Then the resident K, V
-  // times their factors as fp16, into LDS (the kernel copies them on to the
-  // workspace for the dQ kernel at its end, so no wait here covers those
-  // stores).
+  // The group's first block into buffer 0 and zeros into the buffers no
+  // block is copied to before the loop (no product reads a buffer before a
+  // block lands in it: the fill only keeps every stage buffer finite, and
+  // without it the loop's register allocation measured about 1 % slower).
+  // Then the resident K, V times their factors as fp16, into LDS (the
+  // kernel copies them on to the workspace for the dQ kernel at its end,
+  // so no wait here covers those stores).
   if (valid(0)) stage(0, 0);
   for (int b = valid(0) ? 1 : 0; b < 2; ++b)
     for (int i = gt; i < C::kStageBytes / 16; i += 256)
