@@ -270,8 +270,12 @@ void check_fp8(Report& rep, bool launched) {
         const int d = conflict_degree(at, 8);
         if (d > vdeg) vdeg = d;
       }
-  const int lds = 2 * 3 * BN * D;
-  if (lds > 160 * 1024) rep.fail("fwd fp8 D=%d BN=%d: %d bytes of tiles exceed 160 KB", D, BN, lds);
+  // Three K and three V tiles; after the loop the same LDS stages each
+  // wave's 32 output rows (bf16): 8 waves at d = 64, 12 (three groups) at
+  // d = 128.
+  const int tiles = 2 * 3 * BN * D, stage = (D == 128 ? 12 : 8) * 32 * D * 2;
+  const int lds = tiles > stage ? tiles : stage;
+  if (lds > 160 * 1024) rep.fail("fwd fp8 D=%d BN=%d: %d bytes of tiles or staging exceed 160 KB", D, BN, lds);
   rep.note("fwd fp8 D=%d BN=%d (%s): LDS %d B, K read conflict degree %d, V read degree %d", D, BN,
            launched ? "launched" : "not launched", lds, kdeg, vdeg);
 }

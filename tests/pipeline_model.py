@@ -10,7 +10,9 @@ in the loop's own order; `check` then replays them:
   * a read of tile x from buffer b in interval i needs x's copy to have been
     waited for by its issuing group in an interval before i (the barrier
     between then publishes it to every wave);
-  * a read marked unused (its result is thrown away) may see anything.
+  * a read marked unused (its result is thrown away) may see anything;
+  * a group's overwrite of a buffer (output staging) in interval i destroys
+    its tile from i on.
 A wait either drains all of the group's copies or all but those issued in
 the current interval (vmcnt counts in issue order).
 
@@ -23,6 +25,7 @@ from dataclasses import dataclass, field
 @dataclass
 class Interval:
     copies: list = field(default_factory=list)   # (buffer, tile)
+    clobbers: list = field(default_factory=list)  # buffers overwritten with a group's own data
     reads: list = field(default_factory=list)    # (buffer, tile or None for unused)
     wait: str = ""                               # "", "all", "keep_current"
 
@@ -42,6 +45,9 @@ class Group:
 
     def read(self, buf, tile):
         self.cur.reads.append((buf, tile))
+
+    def clobber(self, buf):
+        self.cur.clobbers.append(buf)
 
     def wait(self, kind="all"):
         self.cur.wait = kind
@@ -69,6 +75,10 @@ def check(groups):
                 issued[buf] = i
                 ready.pop(buf, None)
                 pending[gi].append((buf, i))
+            for buf in g.intervals[i].clobbers:
+                content[buf] = ("staged", gi)
+                issued[buf] = i
+                ready.pop(buf, None)
         for gi, g in enumerate(groups):
             for buf, tile in g.intervals[i].reads:
                 if tile is None:
@@ -148,6 +158,56 @@ def forward_schedule(num_kt, preload_v, ahead=3, copy_at="vector", bufs=3, waits
             g.barrier()
         if gi == 0:
             g.barrier()
+    return groups
+
+
+# ---------------------------------------------------------------------------
+# FP8 forward with three groups (12 waves, one wave of each group per SIMD):
+# a step is a matrix phase (P V of tile t with V(t), the scores of tile t + 1
+# with K(t + 1)) and the softmax in two halves, each phase ending at a
+# barrier; group g runs g intervals behind group 0, so at any time one group
+# of each SIMD is in its matrix phase and two in their exponentials.  Group 0
+# copies K tile t + 3 (buffer t % 3) and group 1 V tile t + 2 (buffer
+# (t + 2) % 3) at the start of the first softmax half of step t, each waiting
+# at that half's end for all its copies but that one.  Tiles 0-2 of K and 0-1
+# of V are copied before the first barrier.  After the loop group g passes
+# 2 - g more barriers, then every wave stages its output rows from the start
+# of the LDS (`stage` lists the buffers each group's rows cover).
+# ---------------------------------------------------------------------------
+def fp8_three_group_schedule(num_kt, bufs=3, k_ahead=3, v_ahead=2, stage=(("K0", "K1", "K2", "V0"), ("V1", "V2"), ())):
+    groups = [Group(), Group(), Group()]
+    for gi, g in enumerate(groups):
+        def copy(tensor, t):
+            if t < num_kt:
+                g.copy("%s%d" % (tensor, t % bufs), (tensor, t))
+                return True
+            return False
+        if gi == 0:
+            for t in range(min(k_ahead, num_kt)):
+                copy("K", t)
+        if gi == 1:
+            for t in range(min(v_ahead, num_kt)):
+                copy("V", t)
+        g.wait("all")
+        g.barrier()
+        if num_kt > 0:
+            g.read("K0", ("K", 0))                     # S of tile 0
+        for _ in range(gi):
+            g.barrier()
+        for t in range(num_kt):
+            g.read("V%d" % (t % bufs), ("V", t))
+            if t + 1 < num_kt:
+                g.read("K%d" % ((t + 1) % bufs), ("K", t + 1))
+            g.barrier()
+            if gi in (0, 1):
+                copied = copy("K", t + k_ahead) if gi == 0 else copy("V", t + v_ahead)
+                g.wait("keep_current" if copied else "all")
+            g.barrier()
+            g.barrier()
+        for _ in range(2 - gi):
+            g.barrier()
+        for buf in stage[gi]:
+            g.clobber(buf)
     return groups
 
 

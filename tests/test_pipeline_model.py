@@ -68,6 +68,13 @@ def test_forward_schedule_is_safe(num_kt, preload):
     assert pm.check(pm.forward_schedule(num_kt, preload)) == []
 
 
+@pytest.mark.parametrize("num_kt", range(0, 14))
+def test_fp8_three_group_schedule_is_safe(num_kt):
+    # d = 128 FP8 forward: 12 waves, output rows staged over K0-K2, V0 (group
+    # 0) and V1, V2 (group 1) once every group is past its last tile read.
+    assert pm.check(pm.fp8_three_group_schedule(num_kt)) == []
+
+
 @pytest.mark.parametrize("n_blk", range(0, 12))
 def test_backward_schedules_are_safe(n_blk):
     assert pm.check(pm.dkdv_schedule(n_blk)) == []
@@ -94,6 +101,17 @@ def test_model_catches_planted_schedule_mistakes():
     assert pm.check(pm.forward_schedule(6, True, bufs=2))
     # No wait for the copies: tiles are read before they are known to be in.
     assert pm.check(pm.forward_schedule(6, False, waits=False))
+    # Three groups: K copied four tiles ahead or V three ahead into three
+    # buffers overwrites a tile a later group still reads; two buffers never
+    # suffice.
+    assert pm.check(pm.fp8_three_group_schedule(8, k_ahead=4))
+    assert pm.check(pm.fp8_three_group_schedule(8, v_ahead=3))
+    assert pm.check(pm.fp8_three_group_schedule(8, bufs=2))
+    # Group 0 staging its rows over V0 two intervals before its last
+    # barrier, while group 2 still takes its last P V products from V(6).
+    early = pm.fp8_three_group_schedule(7)
+    early[0].intervals[-4].clobbers.append("V0")
+    assert pm.check(early)
     # The dK/dV kernel's next block copied during the matrix phase, which
     # still reads that buffer's previous block.
     assert pm.check(pm.dkdv_schedule(8, copy_in_vector=False))
