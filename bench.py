@@ -285,7 +285,7 @@ def fp8_step(warmup, steps):
         "tflops": round(tf, 2),
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                     "traffic": measured_traffic("fa_fwd_fp8_kernel", w.name)},
+                     "traffic": measured_traffic("fa_fwd_fp8_g3_kernel", w.name)},
     }
 
 

@@ -506,7 +506,9 @@ fa_fwd_fp8_g3_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ 
   // Under the causal mask the tiles from n_live on hold only keys after
   // every query of this wave: it runs the P V products of tile n_live - 1
   // alone and, on the steps after it, only its copies, waits and barriers.
-  const int n_live = CAUSAL ? min(num_kt, (q_wave0 + 31) / BN + 1) : num_kt;
+  // A wave whose queries all lie past N (the last tile of a head whose N is
+  // not a multiple of 384) has no live step.
+  const int n_live = q_wave0 >= N ? 0 : CAUSAL ? min(num_kt, (q_wave0 + 31) / BN + 1) : num_kt;
   int b0 = 0;
   int t = 0;
   for (; t + 1 < n_live; ++t) {
@@ -523,7 +525,7 @@ fa_fwd_fp8_g3_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ 
     __syncthreads();
     b0 = b1;
   }
-  if (num_kt > 0) {
+  if (n_live > 0) {
     const int b1 = nxt(b0), b2 = nxt(b1);
     matrix_phase_fp8<D, BN, 3, false>(oacc, pb, vbuf(b0), voff, s, kbuf(b0), koff, qb);
     __syncthreads();
