@@ -14,13 +14,15 @@
 //     E4M3's range (448); the running sum l is taken from the fp32 P.  O is
 //     scaled by v_descale / l at the end.
 //
-// Layout (one workgroup = 8 waves = 256 query rows, 64-key tiles):
+// Layout (64-key tiles; d = 64: one workgroup = 8 waves = 256 query rows,
+// d = 128: 12 waves = 384 query rows):
 //   * each wave owns 32 queries; its Q slice (codes) lives in registers as
 //     the B operand of S^T = K Q^T, one query per lane column.
 //   * K and V tiles are copied into LDS straight from global memory
 //     (buffer_load ... lds), three buffers each; waves 0-3 copy K, waves 4-7
-//     V.  The matrix/vector ping-pong of the two wave groups is the bf16
-//     kernel's.
+//     V.  At d = 64 the matrix/vector ping-pong of the two wave groups is
+//     the bf16 kernel's; at d = 128 three groups rotate through a matrix
+//     phase and two softmax halves (fa_fwd_fp8_g3_kernel).
 //   * The 32x32x64 product's k-dimension is any order both operands agree
 //     on.  S^T's row rho of each 32-key block is key kperm(rho) (bits
 //     [a1 a0 h b1 b0] of rho -> [h a1 a0 b1 b0]), so register r of lane half
