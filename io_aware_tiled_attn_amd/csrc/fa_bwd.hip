@@ -384,10 +384,9 @@ __device__ __forceinline__ int build_block_list(int* list, int n, int wave, int 
 // read kLookahead operands ahead of their product, so the read latency
 // hides behind the preceding products.  The stream is the gradient
 // products of the group's previous block, then the two score-side products
-// of its current block.  Scheduling barriers keep it in this order.  Where
-// a group has no previous or no current block, the stream runs anyway: its
-// P and dS registers then hold zeros (the gradient products add nothing)
-// and the scores it computes from a stale buffer are not used.
+// of its current block.  Scheduling barriers keep it in this order.  Either
+// half can run alone (GRADS / SCORES): a wave's first step has no previous
+// block, and the round after its last step no current one.
 constexpr int kLookahead = 8;
 
 // dK/dV kernel.  Operands: per (c, dm) of the gradient products dO^T then
@@ -936,10 +935,10 @@ fa_bwd_dq_kernel(const _Float16* __restrict__ Q16, const _Float16* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) dsw[i] = 0u;
 
-  // The group's first two blocks into buffers 0 and 1; zeros into those of
-  // them the group has no block for.  The products a round runs without a
-  // block need finite operands: buffers 0 and 1 then hold zeros, buffer 2
-  // (read by round 0's gradient product, whose dS is zero) the Q slots.
+  // The group's first two blocks into buffers 0 and 1, zeros into those of
+  // them the group has no block for (no product reads those).  Round 0's
+  // gradient products, whose dS is zero, read buffer 2, which then holds
+  // the Q slots: finite operands.
   if (valid(0)) stage(0, 0);
   if (valid(1)) stage(1, 1);
   for (int b = 0; b < 2; ++b)

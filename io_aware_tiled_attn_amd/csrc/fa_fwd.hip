@@ -507,9 +507,10 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int b_next = b_cur == 2 ? 0 : b_cur + 1;    // (t + 1) % 3
     const int b_after = b_cur == 0 ? 2 : b_cur - 1;   // (t + 2) % 3
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
-    // wave runs the same instruction stream on every step: on causal tiles
-    // wholly above a wave's queries its P is all zero (the tile is masked
-    // like any other).
+    // wave runs the same instruction stream on every step of this loop: on
+    // causal tiles partly above a wave's queries the masked scores give
+    // P = 0 (at d = 128 the tiles wholly above them are the tail after the
+    // loop; at d = 64 they run here too, masked whole).
     matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1).
