@@ -111,6 +111,19 @@ def test_fp8_forward_small(N, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [383, 384, 385, 800])
+def test_fp8_forward_around_query_tiles(N, causal):
+    # d = 128 takes 384 queries per workgroup (three wave groups): N just
+    # below, at and past one tile, and a second tile whose last waves lie
+    # wholly past N, so they run no products.
+    B, H, d = 1, 3, 128
+    announce(f"fp8 forward B{B} H{H} N={N} d={d} causal={causal}")
+    inp = wl.fp8_inputs((B, H, N, d), 9500 + N)
+    o, lse = run(inp, causal)
+    check(inp, causal, o, lse, all_rows(B, H, N), slope_check=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp8_forward_descales_and_scale(causal):
     """Descales far from 1 and an explicit softmax scale: all three fold into
     the kernel's factors."""
