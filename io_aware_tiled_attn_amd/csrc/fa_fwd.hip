@@ -389,7 +389,6 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q_tile_end = min(N, (qt + 1) * C::BM);
   const int key_end = CAUSAL ? q_tile_end : N;
   int num_kt = (key_end + BN - 1) / BN;
-  const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
   auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
   // Sparse: list of visited key tiles, entry = tile | keep(block 0) << 24 |
@@ -460,7 +459,13 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[mb][r] = -INFINITY;
     } else if (masked(t)) {
-      mask_tile<BN>(s, t * BN, qlim, lg);
+      // The lane's last key is rebuilt here, from a lane index the compiler
+      // cannot hoist, rather than held in a register through the loop:
+      // only the tiles on the causal diagonal and the last one get here.
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      const int lim = CAUSAL ? min(q_wave0 + (l & 31), N - 1) : N - 1;
+      mask_tile<BN>(s, t * BN, lim, l >> 5);
     }
   };
 
@@ -493,13 +498,12 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(0), voff, kbuf(1), koff);
   if (group == 1) __syncthreads();
 
-  // Causal, dense, d = 128: visited tiles from n_live on hold only keys
-  // after every query of this wave, so their P is zero.  The wave then runs
-  // the P V products of tile n_live - 1 alone and, on the steps after it,
-  // only the copies, waits and barriers every wave takes part in (skipping
-  // exactly zero terms: the result is the same bit for bit).  At d = 64 the
-  // extra loops cost the registers of the second workgroup per CU.
-  constexpr bool kDeadTail = CAUSAL && !SPARSE && D == 128;
+  // Causal, dense: visited tiles from n_live on hold only keys after every
+  // query of this wave, so their P is zero.  The wave then runs the P V
+  // products of tile n_live - 1 alone and, on the steps after it, only the
+  // copies, waits and barriers every wave takes part in (skipping exactly
+  // zero terms: the result is the same bit for bit).
+  constexpr bool kDeadTail = CAUSAL && !SPARSE;
   const int n_live = kDeadTail ? min(num_kt, (q_wave0 + 31) / BN + 1) : num_kt;
   int b_cur = 0;   // t % 3
   int t = 0;
@@ -509,8 +513,7 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // Phase 1 (matrix cores): O += P(t) V(t); S(t+1) = K(t+1) Q^T.  Every
     // wave runs the same instruction stream on every step of this loop: on
     // causal tiles partly above a wave's queries the masked scores give
-    // P = 0 (at d = 128 the tiles wholly above them are the tail after the
-    // loop; at d = 64 they run here too, masked whole).
+    // P = 0 (the tiles wholly above them are the tail after the loop).
     matrix_phase<D, BN, FWD_LOOKAHEAD, kPreload>(ring, oacc, pb, vbuf(b_cur), voff, s, kbuf(b_next), koff, qb);
     __syncthreads();
     // Phase 2 (vector ALU): P(t+1).
