@@ -312,7 +312,6 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   const int q_tile_end = min(N, (qt + 1) * C::BM);
   const int key_end = CAUSAL ? q_tile_end : N;
   const int num_kt = (key_end + BN - 1) / BN;
-  const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
   auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
   if (num_kt > 0) copy_tile(0, 0);
@@ -322,6 +321,14 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
   if (num_kt > 2) copy_tile(2, 2);
 
   f32x16 s[C::NB];
+  // The lane's last key, rebuilt where a tile is masked (the causal
+  // diagonal and the last tile) from a lane index the compiler cannot
+  // hoist, rather than held in a register through the loop.
+  auto mask_at = [&](int j0) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    mask_tile_fp8<BN>(s, j0, CAUSAL ? min(q_wave0 + (l & 31), N - 1) : N - 1, l >> 5);
+  };
   i32x8 pb[C::NC];
   if (num_kt > 0) {
 #pragma unroll
@@ -331,7 +338,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
 #pragma unroll
       for (int mb = 0; mb < C::NB; ++mb)
         s[mb] = mfma32_fp8(lds_k_operand(kbuf(0) + 32 * mb * D, koff[ks][0], koff[ks][1]), qb[ks], s[mb]);
-    if (masked(0)) mask_tile_fp8<BN>(s, 0, qlim, lg);
+    if (masked(0)) mask_at(0);
     softmax_first_fp8<BN>(s, pb, m_run, l_run, scale_log2);
   }
 
@@ -355,7 +362,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, 
     __syncthreads();
     const bool copy_next = t + 3 < num_kt;
     if (copy_next) copy_tile(t + 3, b_cur);
-    if (masked(t + 1)) mask_tile_fp8<BN>(s, (t + 1) * BN, qlim, lg);
+    if (masked(t + 1)) mask_at((t + 1) * BN);
     softmax_step_fp8<D, BN>(s, pb, m_run, l_run, oacc, scale_log2);
     if (copy_next) wait_vmem_keep<C::kDmaPerWave>();
     else wait_vmem_all();
@@ -460,7 +467,6 @@ fa_fwd_fp8_g3_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ 
   const int q_tile_end = min(N, (qt + 1) * BM);
   const int key_end = CAUSAL ? q_tile_end : N;
   const int num_kt = (key_end + BN - 1) / BN;
-  const int qlim = CAUSAL ? min(q_idx, N - 1) : N - 1;
   auto masked = [&](int t) { return (t * BN + BN > N) || (CAUSAL && t * BN + BN - 1 > q_wave0); };
 
   if (group == 0)
@@ -471,6 +477,14 @@ fa_fwd_fp8_g3_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ 
   __syncthreads();
 
   f32x16 s[C::NB];
+  // The lane's last key, rebuilt where a tile is masked (the causal
+  // diagonal and the last tile) from a lane index the compiler cannot
+  // hoist, rather than held in a register through the loop.
+  auto mask_at = [&](int j0) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    mask_tile_fp8<BN>(s, j0, CAUSAL ? min(q_wave0 + (l & 31), N - 1) : N - 1, l >> 5);
+  };
   i32x8 pb[C::NC];
   if (num_kt > 0) {
 #pragma unroll
@@ -480,7 +494,7 @@ fa_fwd_fp8_g3_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ 
 #pragma unroll
       for (int mb = 0; mb < C::NB; ++mb)
         s[mb] = mfma32_fp8(lds_k_operand(kbuf(0) + 32 * mb * D, koff[ks][0], koff[ks][1]), qb[ks], s[mb]);
-    if (masked(0)) mask_tile_fp8<BN>(s, 0, qlim, lg);
+    if (masked(0)) mask_at(0);
     softmax_first_fp8<BN>(s, pb, m_run, l_run, scale_log2);
   }
   for (int i = 0; i < group; ++i) __syncthreads();
@@ -518,7 +532,7 @@ fa_fwd_fp8_g3_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ 
     matrix_phase_fp8<D, BN, 3>(oacc, pb, vbuf(b0), voff, s, kbuf(b1), koff, qb);
     __syncthreads();
     const bool copied = copy_and_wait(t, b0, b2);
-    if (masked(t + 1)) mask_tile_fp8<BN>(s, (t + 1) * BN, qlim, lg);
+    if (masked(t + 1)) mask_at((t + 1) * BN);
     const float rs0 = tile_exp_fp8<BN, 0, 4>(s, pb, m_run, scale_log2);
     wait_copies(copied);
     __syncthreads();
