@@ -498,13 +498,24 @@ fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if constexpr (kPreload) matrix_preload<D, BN, FWD_LOOKAHEAD>(ring, vbuf(0), voff, kbuf(1), koff);
   if (group == 1) __syncthreads();
 
-  // Causal, dense: visited tiles from n_live on hold only keys after every
-  // query of this wave, so their P is zero.  The wave then runs the P V
+  // Causal (dense, or block-sparse at d = 128, where the 64-key build has
+  // the registers for it): visited tiles from n_live on hold only keys
+  // after every query of this wave, so their P is zero.  The wave then runs the P V
   // products of tile n_live - 1 alone and, on the steps after it, only the
   // copies, waits and barriers every wave takes part in (skipping exactly
   // zero terms: the result is the same bit for bit).
-  constexpr bool kDeadTail = CAUSAL && !SPARSE;
-  const int n_live = kDeadTail ? min(num_kt, (q_wave0 + 31) / BN + 1) : num_kt;
+  constexpr bool kDeadTail = CAUSAL && (!SPARSE || D == 128);
+  int n_live = num_kt;
+  if constexpr (kDeadTail) {
+    // The last key tile holding a key of this wave's queries; visited tiles
+    // come in increasing order, so the dead ones are the list's last few.
+    const int last = (q_wave0 + 31) / BN;
+    if constexpr (SPARSE) {
+      while (n_live > 0 && __builtin_amdgcn_readfirstlane(tile_at(n_live - 1)) > last) --n_live;
+    } else {
+      n_live = min(num_kt, last + 1);
+    }
+  }
   int b_cur = 0;   // t % 3
   int t = 0;
   for (; t + 1 < n_live; ++t) {

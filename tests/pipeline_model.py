@@ -116,7 +116,7 @@ def check(groups):
 # buffer of tile t and waits for everything but that copy at the phase's end.
 # `ahead` = 2 with copy_at = "matrix" is the earlier schedule (tile t + 2
 # copied at the start of the matrix phase, all copies waited for at the end
-# of the vector phase).  Under the causal mask (dense) a bf16 wave skips the
+# of the vector phase).  Under the causal mask a bf16 wave skips the
 # products and softmax of the tiles past its last query but keeps every
 # copy, wait and barrier; dropping reads adds no hazard, so the model keeps
 # them all.
