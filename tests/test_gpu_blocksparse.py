@@ -153,6 +153,20 @@ def test_block_diagonal_equals_independent_blocks():
         assert max_err(to_f64(lse[:, :, r]), to_f64(lb)) <= 1e-4
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse_causal_band(d):
+    """Causal local band + global column over a ragged length: each
+    workgroup's list ends on its own diagonal, where all its waves but the
+    last two have visited tiles past their last query (at d = 128 those are
+    skipped per wave).  Whole heads against the oracle."""
+    shape = (1, 2, 1000, d)
+    announce(f"blocksparse causal band shape={shape}")
+    inp = wl.make_inputs(shape, 7700 + d, "bf16", with_grad=True)
+    mask = wl.local_global_block_mask(1, 2, 1000, band=1)
+    o, lse, grads = run(inp, mask, True)
+    check(inp, mask, True, o, lse, grads, [(0, 0), (0, 1)])
+
+
 def test_sparse_workload_sampled():
     """The benchmark's block-sparse workload (B4 H32 N4096 d128, local band
     + global column) at full size: every output and gradient of three heads
