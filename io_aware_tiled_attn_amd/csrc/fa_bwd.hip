@@ -232,13 +232,25 @@ fa_bwd_convert_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ d
   const __bf16* src[2] = {Q, dO};
   _Float16* dst[2] = {Q16, dO16};
   const int n8 = rows * (D / 8);
+  // All of a thread's loads are issued before its first store, so a chunk
+  // costs one memory round trip rather than one per 16-byte piece.
+  constexpr int kIter = kBwdChunkRows * (D / 8) / 256;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     // The same float kernel 1 computed, so the same factor.
     const float own = pow2_scale_for(part[((size_t)bh * nch + ch) * 4 + t]);
     if (own == f[t]) continue;
-    for (int i = tid; i < n8; i += 256)
-      *(u32x4*)(dst[t] + rbase * D + 8 * (size_t)i) = bf16x8_to_f16x8(*(const u32x4*)(src[t] + rbase * D + 8 * (size_t)i), f[t]);
+    u32x4 x[kIter];
+#pragma unroll
+    for (int j = 0; j < kIter; ++j) {
+      const int i = tid + 256 * j;
+      if (i < n8) x[j] = *(const u32x4*)(src[t] + rbase * D + 8 * (size_t)i);
+    }
+#pragma unroll
+    for (int j = 0; j < kIter; ++j) {
+      const int i = tid + 256 * j;
+      if (i < n8) *(u32x4*)(dst[t] + rbase * D + 8 * (size_t)i) = bf16x8_to_f16x8(x[j], f[t]);
+    }
   }
 }
 
